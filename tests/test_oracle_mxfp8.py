@@ -1,0 +1,121 @@
+"""Pins for the oracle's MXFP8 emulation: the E4M3FN decode table against
+torch's float8_e4m3fn type, rounding against torch's conversion and
+hand-built midpoints, the E8M0 scale rule, group-aware token blocks, and the
+quantised backward against the exact one."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+import moe_inputs as mi
+
+
+def test_decode_table_matches_torch_float8():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    tab = orc.e4m3fn_decode_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(tab))
+    assert nan.sum() == 2                       # 0x7F and 0xFF
+    assert np.array_equal(ref[~nan], tab[~nan])
+    assert tab[0x7E] == 448.0 and tab[0x01] == 2.0 ** -9
+
+
+def test_representable_values_round_trip():
+    tab = orc.e4m3fn_decode_table()
+    codes = np.array([c for c in range(256) if not np.isnan(tab[c])], dtype=np.uint8)
+    enc = orc.e4m3fn_encode(tab[codes])
+    assert np.array_equal(enc, codes)
+
+
+def test_encode_matches_torch_conversion_in_range():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(20000) * 50, rng.standard_normal(20000) * 1e-2,
+                        rng.uniform(-448, 448, 20000)])
+    ours = orc.e4m3fn_encode(v)
+    ref = torch.tensor(v, dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    zero = (orc.e4m3fn_decode_table()[ours] == 0)
+    # torch and we agree on every code (zeros compared by value: +-0 both encode zero)
+    assert np.array_equal(ours[~zero], ref[~zero])
+    assert np.all((ref[zero] & 0x7F) == 0)
+
+
+def test_round_half_to_even_midpoints():
+    # between 1.0 (code 0x38, even) and 1.125 (0x39): midpoint 1.0625 -> 1.0
+    # between 1.125 (0x39) and 1.25 (0x3A, even): midpoint 1.1875 -> 1.25
+    # subnormal: between 0 and 2^-9: 2^-10 -> 0 ; between 2^-9 (odd) and 2^-8 (even) -> 2^-8
+    v = np.array([1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9, -1.0625, 464.0, 1e6, -1e6])
+    enc = orc.e4m3fn_encode(v)
+    assert enc.tolist() == [0x38, 0x3A, 0x00, 0x02, 0xB8, 0x7E, 0x7E, 0xFE]
+
+
+def test_scale_rule():
+    amax = np.array([448.0, 448.00001, 224.0, 224.0001, 1.0, 0.0, 3.5, 1e-30, 2.0 ** 130])
+    X = orc.mx_scale_exponent(amax)
+    assert X.tolist()[:5] == [0, 1, -1, 0, -8]
+    assert X[5] == -127
+    # property: amax / 2^X in (224, 448] whenever no clamp applies
+    rng = np.random.default_rng(1)
+    a = np.exp(rng.uniform(-40, 40, 5000))
+    X = orc.mx_scale_exponent(a)
+    ratio = a / np.exp2(X.astype(np.float64))
+    assert np.all(ratio <= 448.0) and np.all(ratio > 224.0)
+    assert X[-1] <= 127 and orc.mx_scale_exponent(np.array([2.0 ** 130]))[0] == 122
+
+
+def test_block_quant_error_bound():
+    """Each element is within half an E4M3 step (relative 2^-4) of its block-scaled value,
+    or within the subnormal step 2^-10 * 2^X."""
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-5, 5, (64, 1)))
+    deq, codes, X = orc.mx_quant_dequant(a, axis=1)
+    scale = np.repeat(np.exp2(X.astype(np.float64)), 32, axis=1)
+    err = np.abs(deq - a)
+    bound = np.maximum(np.abs(a) * 2.0 ** -4, 2.0 ** -10 * scale)
+    assert np.all(err <= bound * (1 + 1e-12))
+    # quantising the dequantised array again is exact (idempotent)
+    deq2, _, _ = orc.mx_quant_dequant(deq, axis=1)
+    assert np.array_equal(deq, deq2)
+
+
+def test_group_aware_token_blocks():
+    rng = np.random.default_rng(3)
+    offsets = np.array([0, 5, 5, 70, 100])       # segments of 5, 0, 65, 30 rows
+    a = rng.standard_normal((100, 64))
+    a[5:70] *= 1000.0                            # a loud segment must not change its neighbours
+    q = orc.mx_quant_dequant_tokens(a, offsets)
+    for lo, hi in ((0, 5), (70, 100)):
+        seg = np.zeros(((hi - lo + 31) // 32 * 32, 64))
+        seg[:hi - lo] = a[lo:hi]
+        ref, _, _ = orc.mx_quant_dequant(seg, axis=0)
+        assert np.array_equal(q[lo:hi], ref[:hi - lo])
+    # rows 5..36 form one block, 37..68 the next, 69 a block of its own
+    single, _, _ = orc.mx_quant_dequant(np.vstack([a[69:70], np.zeros((31, 64))]), axis=0)
+    assert np.array_equal(q[69], single[0])
+
+
+def test_quantised_backward_close_to_exact():
+    d = mi.LayerDims(T=128, H=128, I=64, E=4, k=2, dtype="bf16", mode="fp8_bwd")
+    inp = mi.make_inputs(d, 5)
+    r = orc.route(inp["logits"], d.k)
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    g = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    q = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    for key in ("dx", "dw13", "dw2", "dgate", "dlogits"):
+        rel = np.max(np.abs(q[key] - g[key])) / np.max(np.abs(g[key]))
+        assert 1e-4 < rel < 0.15, (key, rel)     # quantisation is visible but bounded
+
+
+def test_quantised_backward_structure_with_identity_quantiser(monkeypatch):
+    """With the quantiser replaced by the identity the fp8_bwd backward must equal
+    the exact backward: this pins which operands meet in which GEMM."""
+    d = mi.LayerDims(T=96, H=64, I=32, E=5, k=2, dtype="fp32")
+    inp = mi.make_inputs(d, 6)
+    r = orc.route(inp["logits"], d.k)
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    g = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    monkeypatch.setattr(orc, "mx_quant_dequant", lambda a, axis=-1: (np.asarray(a, np.float64), None, None))
+    monkeypatch.setattr(orc, "mx_quant_dequant_tokens", lambda a, offsets: np.asarray(a, np.float64))
+    q = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    for key in ("dx", "dw13", "dw2", "dgate", "dlogits"):
+        rel = np.max(np.abs(q[key] - g[key])) / np.max(np.abs(g[key]))
+        assert rel < 1e-12, (key, rel)
