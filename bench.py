@@ -1,0 +1,206 @@
+"""Benchmark of the MoE expert layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--cpu-tokens 4096] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+route + forward + backward of the layer (Qwen3-30B-A3B expert shape by
+default: T=16384, H=2048, I=768, E=128, top-8, bf16).  Inputs are resident in
+HBM before the timed region.  Prints one JSON line.
+
+value = algorithmic GEMM FLOPs of forward + backward (18*M*H*I, M = T*k)
+divided by the step time, in TFLOP/s.  Per-kernel durations come from HIP
+events recorded between the library's kernels over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd ms & TFLOPS, Qwen3-30B-A3B shape T=16384; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
+BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            arr[i] = h
+        return arr
+
+    def elapsed(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def gemm_flops(d):
+    MHI = d.M * d.H * d.I
+    return {"gemm1_swiglu": 4 * MHI, "gemm2": 2 * MHI, "dgrad2_dswiglu": 2 * MHI, "dgrad1": 4 * MHI,
+            "wgrad2": 2 * MHI, "wgrad1": 4 * MHI}
+
+
+def hbm_bytes(d):
+    """Algorithmic HBM bytes of the memory-bound kernels (bf16 rows)."""
+    rows = d.M * d.H * 2 + d.T * d.H * 2
+    return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4}
+
+
+def cpu_baseline(d, inp, n_tokens):
+    """The fp64 oracle on the first n_tokens tokens of the same batch (all experts)."""
+    import numpy as np
+    from oracle import moe_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    n = min(n_tokens, d.T)
+    x, L, dy = inp["x"][:n], inp["logits"][:n], inp["dy"][:n]
+    t0 = time.perf_counter()
+    r = orc.route(L, d.k)
+    Y, st = orc.forward(x, inp["w13"], inp["w2"], r)
+    orc.backward(dy, x, inp["w13"], inp["w2"], r, st)
+    dt = time.perf_counter() - t0
+    flops = 18.0 * n * d.k * d.H * d.I
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, route+forward+backward of the first {n} of {d.T} tokens "
+                      f"(all {d.E} experts, same weights), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X and has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import moe_inputs as mi
+    import grouped_gemm_layer_amd as g
+
+    d = mi.CONFIGS[args.config]
+    seed = args.config if args.seed is None else args.seed
+    print(f"[bench] config {args.config}: {mi.CONFIG_NAMES[args.config]}", file=sys.stderr, flush=True)
+    inp = mi.make_inputs(d, seed)
+    torch.cuda.set_device(0)
+    layer = g.MoeLayer(d.T, d.H, d.I, d.E, d.k, mode=d.run_mode)
+    adt = layer.act_dtype
+    dev = lambda a, dt: torch.from_numpy(a).to(device="cuda", dtype=dt)
+    x, w13, w2, dy = dev(inp["x"], adt), dev(inp["w13"], adt), dev(inp["w2"], adt), dev(inp["dy"], adt)
+    logits = dev(inp["logits"], torch.float32)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    nf, nb = g.num_kernels("forward"), g.num_kernels("backward")
+    K, W = args.steps, args.warmup
+    fev = [ev.create(nf + 1) for _ in range(K)]
+    bev = [ev.create(nb + 1) for _ in range(K)]
+    rstart = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    rend = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+
+    def step(i=None):
+        if i is None:
+            layer.route(logits)
+            layer.forward(x, w13, w2)
+            layer.backward(dy, x, w13, w2)
+        else:
+            rstart[i].record()
+            layer.route(logits)
+            rend[i].record()
+            layer.forward(x, w13, w2, events=fev[i])
+            layer.backward(dy, x, w13, w2, events=bev[i])
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    names = FWD_KERNELS + BWD_KERNELS
+    per = {n: [] for n in names}
+    fwd_ms, bwd_ms, route_ms = [], [], []
+    for i in range(K):
+        for j in range(nf):
+            per[FWD_KERNELS[j]].append(ev.elapsed(fev[i][j], fev[i][j + 1]))
+        for j in range(nb):
+            per[BWD_KERNELS[j]].append(ev.elapsed(bev[i][j], bev[i][j + 1]))
+        fwd_ms.append(ev.elapsed(fev[i][0], fev[i][nf]))
+        bwd_ms.append(ev.elapsed(bev[i][0], bev[i][nb]))
+        route_ms.append(rstart[i].elapsed_time(rend[i]))
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    flops = gemm_flops(d)
+    hbm = hbm_bytes(d)
+    kernels = {}
+    for n in names:
+        ent = {"ms": round(avg[n], 4)}
+        if n in flops:
+            tf = flops[n] / (avg[n] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        if n in hbm:
+            gbs = hbm[n] / (avg[n] * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[n] = ent
+    total_flops = 18.0 * d.M * d.H * d.I
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(flops, key=lambda n: avg[n])
+    dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
+    gemm_ms = sum(avg[n] for n in flops)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if d.run_mode != "fp32" else "f32", "data": "synthetic",
+        "config": {"workload": mi.CONFIG_NAMES[args.config], "T": d.T, "H": d.H, "I": d.I, "E": d.E,
+                   "k": d.k, "mode": d.run_mode, "seed": seed},
+        "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "route_ms": round(float(np.mean(route_ms)), 4),
+        "fwd_tflops": round(6.0 * d.M * d.H * d.I / (np.mean(fwd_ms) * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(12.0 * d.M * d.H * d.I / (np.mean(bwd_ms) * 1e-3) / 1e12, 1),
+        "gemm_tflops": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_mfma_frac": round(total_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels, "roofline": roofline, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+// Combine (forward) and unpermute-reduce (backward), and the router backward.
+//
+// Combine returns the expert rows to token order and sums the results of the
+// token's experts (TE dropless-MoE page, "Optimisation 2: dispatch and combine
+// via NCCL EP"), here weighted by the gates:
+//   out[t] = sum_{j=0..k-1} gate[t,j] * rows[f2s[t*k+j]]    (fp32, slot order)
+// With gate == nullptr the weights are 1 (the backward's dX reduction).
+// One block per token, 16-byte vectors per thread: HBM-bound row traffic,
+// deterministic (no atomics).
+#include "moe_internal.h"
+
+namespace moe {
+
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> { static constexpr int N = 8; };
+template <> struct Vec16<float> { static constexpr int N = 4; };
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows, const int32_t* __restrict__ f2s,
+                                                      const float* __restrict__ gate, int k, int H,
+                                                      T* __restrict__ out) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ int s_row[32];
+  __shared__ float s_g[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = f2s[(size_t)t * k + threadIdx.x];
+    s_g[threadIdx.x] = gate ? gate[(size_t)t * k + threadIdx.x] : 1.0f;
+  }
+  __syncthreads();
+  for (int h0 = threadIdx.x * V; h0 < H; h0 += 256 * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(rows + (size_t)s_row[j] * H + h0);
+      const float g = s_g[j];
+      if constexpr (V == 8) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += g * __uint_as_float(w[i] << 16);
+          acc[2 * i + 1] += g * __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else {
+        acc[0] += g * __uint_as_float(raw.x);
+        acc[1] += g * __uint_as_float(raw.y);
+        acc[2] += g * __uint_as_float(raw.z);
+        acc[3] += g * __uint_as_float(raw.w);
+      }
+    }
+    uint4 o;
+    if constexpr (V == 8) {
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+    } else {
+      o.x = __float_as_uint(acc[0]);
+      o.y = __float_as_uint(acc[1]);
+      o.z = __float_as_uint(acc[2]);
+      o.w = __float_as_uint(acc[3]);
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + h0) = o;
+  }
+}
+
+template <typename T>
+hipError_t launch_combine(const T* rows, const int32_t* f2s, const float* gate, int Tn, int k, int H, T* out,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel<T>, dim3(Tn), dim3(256), 0, s, rows, f2s, gate, k, H, out);
+  return hipGetLastError();
+}
+template hipError_t launch_combine<bf16_t>(const bf16_t*, const int32_t*, const float*, int, int, int, bf16_t*,
+                                           hipStream_t);
+template hipError_t launch_combine<float>(const float*, const int32_t*, const float*, int, int, int, float*,
+                                          hipStream_t);
+
+// Router backward, one wave per token:
+//   dgate[t,j] = sum_p dgate_part[p][row of slot j]      (p ascending)
+//   dlogits[t,e] = gate_j (dgate_j - sum_i gate_i dgate_i) if e = idx[t,j], else 0
+// (softmax over the selected logits, differentiated).
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ part, int n_parts,
+                                                         const int32_t* __restrict__ f2s,
+                                                         const float* __restrict__ gate,
+                                                         const int32_t* __restrict__ idx, int Tn, int k, int E,
+                                                         int M, float* __restrict__ dgate,
+                                                         float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  float dg = 0.f, g = 0.f;
+  int e = -1;
+  if (lane < k) {
+    const size_t f = (size_t)t * k + lane;
+    const int r = f2s[f];
+    for (int p = 0; p < n_parts; ++p) dg += part[(size_t)p * M + r];
+    g = gate[f];
+    e = idx[f];
+    dgate[f] = dg;
+  }
+  float inner = g * dg;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) inner += __shfl_xor(inner, off);
+  if (dlogits == nullptr) return;
+  const float mine = g * (dg - inner);
+  float* row = dlogits + (size_t)t * E;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int ee = e0 + lane;
+    float val = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(e, j);
+      const float vj = __shfl(mine, j);
+      if (ej == ee) val = vj;
+    }
+    if (ee < E) row[ee] = val;
+  }
+}
+
+hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t* f2s, const float* gate,
+                             const int32_t* topk_idx, int Tn, int k, int E, int M, float* dgate, float* dlogits,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((Tn + 3) / 4), dim3(256), 0, s, dgate_part, n_parts, f2s, gate,
+                     topk_idx, Tn, k, E, M, dgate, dlogits);
+  return hipGetLastError();
+}
+
+}  // namespace moe

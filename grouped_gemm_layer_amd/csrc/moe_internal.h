@@ -1,0 +1,128 @@
+// Internal declarations shared by the HIP translation units of the MoE layer
+// library (kernels and the C-ABI layer).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Element types.  bf16 values travel as raw 16-bit patterns.
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+// Two floats -> packed pair of bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct ElemTraits<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------------------
+// SwiGLU and its derivative, fp32.
+//   A = SiLU(g1) * g3,  SiLU(z) = z * sigmoid(z)
+//   dg1 = dA * g3 * s * (1 + g1 (1 - s)),  dg3 = dA * SiLU(g1)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Problem description handed to every GEMM launcher.
+// ---------------------------------------------------------------------------
+struct LayerArgs {
+  int T, H, I, E, k, M;
+  // routing (device)
+  const int32_t* offsets;         // [E+1]
+  const int32_t* s2f;             // [M]
+  const int32_t* f2s;             // [M]
+  const float* gate;              // [T*k] flat
+  // tile table for row-ragged GEMMs (device, written by build_tile_table)
+  const int32_t* tile_expert;     // [max_tiles]
+  const int32_t* tile_row0;       // [max_tiles]
+  // inputs
+  const void* x;                  // [T,H]
+  const void* w13;                // [E,2I,H]
+  const void* w2;                 // [E,H,I]
+  const void* dy;                 // [T,H]
+  // forward intermediates / outputs
+  void* G13;                      // [M,2I]  (saved)
+  void* A;                        // [M,I]
+  void* O;                        // [M,H]
+  // backward intermediates / outputs
+  void* dG13;                     // [M,2I]
+  void* Ag;                       // [M,I]   gate * A
+  void* dXp;                      // [M,H]
+  float* dgate_part;              // [n_parts, M]
+  float* dw13;                    // [E,2I,H]
+  float* dw2;                     // [E,H,I]
+};
+
+// Number of M tiles of height bm over all experts is at most this bound.
+inline int max_row_tiles(int M, int E, int bm) { return (M + bm - 1) / bm + E; }
+
+// GEMM kinds of the layer.
+enum GemmKind {
+  KIND_FWD1 = 0,   // G13 = Xp W13^T, SwiGLU epilogue -> G13 (saved), A
+  KIND_FWD2 = 1,   // O = A W2^T
+  KIND_DGRAD2 = 2, // dA' = dYp W2; epilogue: dgate partials, Ag, dSwiGLU -> dG13
+  KIND_DGRAD1 = 3, // dXp = dG13 W13
+  KIND_WGRAD2 = 4, // dW2[e] = dYp^T Ag     (K = rows of e)
+  KIND_WGRAD1 = 5  // dW13[e] = dG13^T Xp   (K = rows of e)
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() of its launch).
+// ---------------------------------------------------------------------------
+// routing
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* gate,
+                        int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
+                        int32_t* ws_partials, int32_t* ws_bases, hipStream_t s);
+int route_num_blocks(int M);   // blocks of the histogram / scatter passes
+
+hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles,
+                             int32_t* tile_expert, int32_t* tile_row0, hipStream_t s);
+
+// combine / unpermute-reduce (fp32 accumulate in slot order)
+template <typename T>
+hipError_t launch_combine(const T* rows, const int32_t* f2s, const float* gate, int Tn, int k, int H,
+                          T* out, hipStream_t s);
+// router backward: dgate from per-N-tile partials, then the logit gradient
+hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t* f2s,
+                             const float* gate, const int32_t* topk_idx, int Tn, int k, int E, int M,
+                             float* dgate, float* dlogits, hipStream_t s);
+
+// GEMMs
+hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s);
+hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s);
+
+// tiling constants the API layer needs for workspace sizing
+constexpr int BF16_BM = 128;     // rows (tokens) per tile of the row-ragged bf16 GEMMs
+constexpr int BF16_BN = 128;
+constexpr int FP32_BM = 64;
+constexpr int FP32_BN = 64;
+inline int dgrad2_parts(bool bf16, int I) {
+  // N tiles of the dgrad of W2 (N = I): one partial per tile for the gate gradient
+  return bf16 ? (I + BF16_BN - 1) / BF16_BN : (I + FP32_BN - 1) / FP32_BN;
+}
+
+}  // namespace moe

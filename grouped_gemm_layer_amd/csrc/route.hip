@@ -1,0 +1,234 @@
+// Routing kernels: top-k + gates, expert histogram, expert-major scan, stable
+// scatter into the expert-sorted order, and the ragged tile table.
+//
+// What is computed (TE dropless-MoE page, "01" and "03": the router assigns
+// each token to a few experts and every token is kept; "Optimisation 1": the
+// per-expert token counts stay on the device):
+//   idx[t, j]  = j-th largest logit of token t, key (-logit, expert id)
+//   gate[t, j] = softmax over the k selected logits
+//   counts, offsets, and the stable sort of flat slots t*k+j by expert.
+// All integer results are bit-exact and independent of scheduling: LDS
+// atomics only count (order-free), and ranks come from wave ballots.
+#include "moe_internal.h"
+
+#include <math.h>
+
+namespace moe {
+
+constexpr int ROUTE_CHUNK = 4096;   // flat slots per block of the histogram / scatter
+constexpr int MAX_EPL = 8;          // logits per lane: E <= 512
+constexpr int MAX_E = 512;
+
+int route_num_blocks(int M) { return (M + ROUTE_CHUNK - 1) / ROUTE_CHUNK; }
+
+// One wave per token, four tokens per block.
+__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits, int T, int E,
+                                                        int k, int32_t* __restrict__ idx,
+                                                        float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // whole waves leave; no block barrier follows
+  const float* row = logits + (size_t)t * E;
+  float v[MAX_EPL];
+  uint32_t live = 0;
+#pragma unroll
+  for (int q = 0; q < MAX_EPL; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = 0.f;
+    if (e < E) { v[q] = row[e]; live |= 1u << q; }
+  }
+  float my_v = 0.f, v0 = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    // best (largest value, then smallest id) among this lane's live entries
+    float bv = 0.f;
+    int be = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < MAX_EPL; ++q) {
+      if (live & (1u << q)) {
+        const int e = lane + 64 * q;
+        if (be == INT_MAX || v[q] > bv || (v[q] == bv && e < be)) { bv = v[q]; be = e; }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
+    }
+    if (lane == (be & 63)) live &= ~(1u << (be >> 6));
+    if (j == 0) v0 = bv;
+    if (lane == j) { my_v = bv; my_e = be; }
+  }
+  float ex = (lane < k) ? expf(my_v - v0) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    gate[(size_t)t * k + lane] = ex / sum;
+  }
+}
+
+// Per-block expert histogram of ROUTE_CHUNK flat slots.
+__global__ __launch_bounds__(256) void expert_hist_kernel(const int32_t* __restrict__ idx, int M, int E,
+                                                          int32_t* __restrict__ partials) {
+  __shared__ int s_hist[MAX_E];
+  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * ROUTE_CHUNK;
+  for (int i = threadIdx.x; i < ROUTE_CHUNK; i += 256) {
+    const int f = base + i;
+    if (f < M) atomicAdd(&s_hist[idx[f]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) partials[blockIdx.x * E + e] = s_hist[e];
+}
+
+// One block: counts, offsets and the expert-major block bases
+//   bases[b][e] = offsets[e] + sum_{b' < b} partials[b'][e].
+__global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __restrict__ partials, int nblk,
+                                                           int E, int32_t* __restrict__ bases,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int s_scan[2][MAX_E];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = partials[b * E + e];
+      bases[b * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+  }
+  // inclusive Hillis-Steele scan over experts
+  int cur = 0;
+  if (e < MAX_E) s_scan[0][e] = (e < E) ? run : 0;
+  __syncthreads();
+  for (int off = 1; off < MAX_E; off <<= 1) {
+    if (e < MAX_E) {
+      int val = s_scan[cur][e];
+      if (e >= off) val += s_scan[cur][e - off];
+      s_scan[cur ^ 1][e] = val;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int excl = s_scan[cur][e] - run;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = s_scan[cur][e];
+    for (int b = 0; b < nblk; ++b) bases[b * E + e] += excl;
+  }
+}
+
+// Stable scatter: slot f of expert e goes to bases[b][e] + (number of earlier
+// slots of the same block routed to e).  Earlier = smaller flat index.
+__global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* __restrict__ idx, int M, int E,
+                                                             int ebits, const int32_t* __restrict__ bases,
+                                                             int32_t* __restrict__ s2f,
+                                                             int32_t* __restrict__ f2s) {
+  __shared__ int s_run[MAX_E];
+  __shared__ int s_wc[4][MAX_E];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    s_run[e] = bases[blockIdx.x * E + e];
+    s_wc[0][e] = s_wc[1][e] = s_wc[2][e] = s_wc[3][e] = 0;
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = blockIdx.x * ROUTE_CHUNK;
+  for (int round = 0; round < ROUTE_CHUNK / 256; ++round) {
+    const int f = base + round * 256 + threadIdx.x;
+    const bool valid = f < M;
+    const int e = valid ? idx[f] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (valid && rank == 0) s_wc[wave][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = s_run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wc[w][e];
+      s2f[pos] = f;
+      f2s[f] = pos;
+    }
+    __syncthreads();
+    for (int ee = threadIdx.x; ee < E; ee += 256) {
+      s_run[ee] += s_wc[0][ee] + s_wc[1][ee] + s_wc[2][ee] + s_wc[3][ee];
+      s_wc[0][ee] = s_wc[1][ee] = s_wc[2][ee] = s_wc[3][ee] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* gate,
+                        int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
+                        int32_t* ws_partials, int32_t* ws_bases, hipStream_t s) {
+  const int M = T * k;
+  const int nblk = route_num_blocks(M);
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  hipLaunchKernelGGL(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, gate);
+  hipLaunchKernelGGL(expert_hist_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, M, E, ws_partials);
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, ws_partials, nblk, E, ws_bases,
+                     counts, offsets);
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, M, E, ebits, ws_bases,
+                     s2f, f2s);
+  return hipGetLastError();
+}
+
+// Tile table of the row-ragged GEMMs: tile i covers rows [row0, row0 + bm) of
+// expert tile_expert[i] (clipped to the expert's end); unused tiles get -1.
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm,
+                                                          int max_tiles, int32_t* __restrict__ tile_expert,
+                                                          int32_t* __restrict__ tile_row0) {
+  __shared__ int s_start[2][MAX_E + 1];
+  const int e = threadIdx.x;
+  int cur = 0;
+  int nt = 0;
+  if (e < E) nt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  if (e <= MAX_E) s_start[0][e] = (e < E) ? nt : 0;
+  __syncthreads();
+  for (int off = 1; off <= MAX_E; off <<= 1) {
+    if (e <= MAX_E) {
+      int val = s_start[cur][e];
+      if (e >= off) val += s_start[cur][e - off];
+      s_start[cur ^ 1][e] = val;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
+  const int total = s_start[cur][E - 1];
+  for (int t = threadIdx.x; t < max_tiles; t += 1024) {
+    int ex = -1, r0 = 0;
+    if (t < total) {
+      int lo = 0, hi = E - 1;            // first e with inclusive(e) > t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[cur][mid] > t) hi = mid; else lo = mid + 1;
+      }
+      ex = lo;
+      const int first = (lo == 0) ? 0 : s_start[cur][lo - 1];
+      r0 = offsets[lo] + (t - first) * bm;
+    }
+    tile_expert[t] = ex;
+    tile_row0[t] = r0;
+  }
+}
+
+hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles, int32_t* tile_expert,
+                             int32_t* tile_row0, hipStream_t s) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
+                     tile_row0);
+  return hipGetLastError();
+}
+
+}  // namespace moe

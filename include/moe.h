@@ -1,0 +1,159 @@
+/*
+ * moe.h -- C ABI of the fused, dropless mixture-of-experts expert layer for
+ * training on one MI355X (gfx950).
+ *
+ * The layer (one GPU's share of the work):
+ *   forward : top-k routing -> permute token rows into expert-contiguous order
+ *             -> grouped GEMM with W1/W3 and a SwiGLU epilogue -> grouped GEMM
+ *             with W2 -> gate-weighted combine back to token order;
+ *   backward: combine-backward -> SwiGLU derivative -> grouped dgrad/wgrad
+ *             GEMMs of the three expert matrices -> routing-weight gradient.
+ * Sources: Prime Mega MoE news page, "How does the fused kernel work?" (one
+ * call fusing dispatch, the two expert linear layers, SwiGLU and combine;
+ * GPU-only scratch buffers instead of intermediate tensors; BF16/MXFP8 and an
+ * fp8_bwd mode, BF16 forward with FP8 backward); TE dropless-MoE page,
+ * "03 Specialised optimisations" and "Optimisation 1: Grouped GEMM" (no
+ * token dropping or padding; grouped GEMM over the actual per-expert counts,
+ * which stay on the device so that nothing waits on a device-to-host copy);
+ * neurobober digest, "Overlapping Backward Pass" (activation gradients need
+ * the expert weights, not the weight gradients).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument named as "device" is a device pointer; dims and
+ *     routing structs are host pointers read during the call only.
+ *   - The caller owns all memory.  The library allocates nothing and keeps no
+ *     global state; calls with distinct workspaces may run concurrently.
+ *   - Every call only enqueues work on `stream` (no host synchronisation, no
+ *     device-to-host copy), so a call may be captured in a HIP graph.
+ *   - Validation happens on the host before any launch.  A non-zero status
+ *     means nothing was enqueued.  Launch errors map to MOE_ERR_LAUNCH.
+ *   - Device pointers must be 256-byte aligned; buffers may not alias.
+ *   - Results are deterministic: bitwise identical for identical inputs.
+ *
+ * Shapes: T tokens, H hidden, I expert intermediate, E experts, k experts per
+ * token, M = T*k routed rows.  Activations and weights are row-major:
+ *   x, dy, y, dx [T,H];  w13 [E,2I,H] (rows [0,I) = W1, [I,2I) = W3);
+ *   w2 [E,H,I];  logits [T,E] fp32;  dw13 [E,2I,H] fp32;  dw2 [E,H,I] fp32.
+ * Element type of x/dy/y/dx/w13/w2: fp32 in MOE_MODE_FP32, bf16 (raw 16-bit
+ * patterns) otherwise.  Gates, gate/logit gradients and weight gradients are
+ * always fp32.  Current limits: H and I multiples of 64, E <= 512, k <= 32.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_MODE_FP32 = 0,     /* fp32 activations/weights (debug and tiny shapes) */
+  MOE_MODE_BF16 = 1,     /* bf16 storage, fp32 accumulation, MFMA GEMMs */
+  MOE_MODE_MXFP8 = 2,    /* reserved: MXFP8 forward and backward (not yet built) */
+  MOE_MODE_FP8_BWD = 3   /* bf16 forward, MXFP8 backward (not yet built) */
+} moe_mode;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL */
+  MOE_ERR_DIMS = 2,         /* a dimension <= 0, k > E, or sizes overflow */
+  MOE_ERR_UNSUPPORTED = 3,  /* valid but outside this build's limits (mode, H/I % 64, E, k) */
+  MOE_ERR_ALIGN = 4,        /* a device pointer is not 256-byte aligned */
+  MOE_ERR_WORKSPACE = 5,    /* workspace smaller than moe_workspace_size reports */
+  MOE_ERR_LAUNCH = 6        /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+typedef struct {
+  int32_t T, H, I, E, k;
+  int32_t mode;             /* a moe_mode value */
+} moe_dims;
+
+/* Routing state produced by moe_route and consumed by forward/backward.  All
+ * members are device pointers owned by the caller. */
+typedef struct {
+  int32_t* topk_idx;        /* [T,k] expert of slot j of token t (slot 0 = largest logit) */
+  float* gate;              /* [T,k] renormalised softmax over the k selected logits */
+  int32_t* counts;          /* [E]   rows routed to each expert */
+  int32_t* offsets;         /* [E+1] exclusive prefix sum of counts; offsets[E] = M */
+  int32_t* sorted_to_flat;  /* [M]   row r of the expert-sorted order -> flat slot t*k+j */
+  int32_t* flat_to_sorted;  /* [M]   inverse permutation */
+} moe_routing;
+
+/* Sizes in bytes of the buffers the caller provides (host-only, pure).
+ *   route_ws : workspace of moe_route
+ *   saved    : state written by moe_forward and read by moe_backward
+ *   fwd_ws   : workspace of moe_forward
+ *   bwd_ws   : workspace of moe_backward
+ * Any output pointer may be NULL. */
+moe_status moe_workspace_size(const moe_dims* dims, size_t* route_ws, size_t* saved,
+                              size_t* fwd_ws, size_t* bwd_ws);
+
+/* Top-k routing (TE dropless-MoE page, "01": the router sends each token to a
+ * few experts; Prime Mega MoE news page, "Short": top-8 of 128).
+ * For each token the k largest logits are chosen, ordered by (-logit, expert
+ * id) so that ties go to the smaller id; gate = softmax over the k selected
+ * logits.  counts/offsets/maps describe the stable sort of the flat slots by
+ * expert (rows of one expert are in ascending token order).  Bit-exact and
+ * deterministic.  logits: device [T,E] fp32, finite values. */
+moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward pass (Prime Mega MoE news page, "How does the fused kernel work?").
+ *   G13[r] = x[t(r)] W13[e]^T,  A = SiLU(G1) * G3,  O = A W2[e]^T   (per expert e)
+ *   y[t]   = sum_j gate[t,j] * O[flat_to_sorted[t*k+j]]               (fp32 sum in slot order)
+ * x, w13, w2: device inputs; y: device output [T,H]; saved: device buffer of
+ * the size reported (G13 of every routed row), to be passed unchanged to
+ * moe_backward. */
+moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                       const moe_routing* routing, void* y, void* saved,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward pass of <dy, y> (neurobober digest, "Overlapping Backward Pass":
+ * the activation-gradient chain needs only the weights; the weight gradients
+ * are independent of it).
+ *   dA'  = dy[t(r)] W2[e];  dgate[t,j] = <dA'_r, A_r>;  dA = gate * dA'
+ *   dG1  = dA * G3 * s * (1 + G1 (1 - s)),  dG3 = dA * SiLU(G1),  s = sigmoid(G1)
+ *   dx[t] = sum_j (dG13 W13[e])[row of slot j]       (fp32 sum in slot order)
+ *   dw2[e]  = sum_r dy[t(r)]^T (gate_r A_r)          (fp32 accumulate and output)
+ *   dw13[e] = sum_r dG13_r^T x[t(r)]                 (fp32; zero for an empty expert)
+ *   dlogits[t,e] = gate_e (dgate_e - sum_j gate_j dgate_j) on the top-k set, else 0
+ * dy, x, w13, w2: device inputs; saved: from moe_forward; dx: device [T,H];
+ * dw13, dw2: device fp32, overwritten; dgate: device [T,k] fp32; dlogits:
+ * device [T,E] fp32 or NULL to skip. */
+moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, const void* w13,
+                        const void* w2, const moe_routing* routing, const void* saved,
+                        void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Benchmarking variants of moe_forward / moe_backward: the same work, and in
+ * addition events[0] is recorded on `stream` before the first kernel and
+ * events[i+1] after kernel i, so that hipEventElapsedTime(events[i],
+ * events[i+1]) is the duration of kernel i.  `events` is a host array of
+ * n_events >= moe_num_kernels(...) + 1 events created by the caller
+ * (MOE_ERR_NULL / MOE_ERR_DIMS otherwise).  Kernel order:
+ *   forward : tile table, GEMM W13 + SwiGLU, GEMM W2, combine
+ *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
+ *             unpermute-reduce, router backward, wgrad W2, wgrad W13 */
+moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                             const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
+                             hipStream_t stream, hipEvent_t* events, int n_events);
+moe_status moe_backward_timed(const moe_dims* dims, const void* dy, const void* x, const void* w13,
+                              const void* w2, const moe_routing* routing, const void* saved, void* dx,
+                              float* dw13, float* dw2, float* dgate, float* dlogits, void* ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t* events, int n_events);
+
+/* Number of kernels a call launches: which = 0 route, 1 forward, 2 backward
+ * (-1 for any other value).  Host-only. */
+int moe_num_kernels(int which);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

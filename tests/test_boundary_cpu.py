@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moe.h declares, sizes its workspaces consistently, and
+rejects invalid calls with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import grouped_gemm_layer_amd as g
+    if not os.path.exists(g.lib_path()):
+        pytest.fail("libmoe_gfx950.so is not built (python -m grouped_gemm_layer_amd.build_lib)")
+    return g, g.load_library()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    g, lib = _lib()
+    names = _declared_functions()
+    assert set(names) >= {"moe_workspace_size", "moe_route", "moe_forward", "moe_backward", "moe_status_str"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    g, lib = _lib()
+    for st in range(7):
+        assert len(g.status_str(st)) > 0
+
+
+def test_workspace_sizes_scale():
+    g, lib = _lib()
+    d = g.Dims.of(16384, 2048, 768, 128, 8, "bf16")
+    rws, saved, fws, bws = g.workspace_size(d)
+    M = 16384 * 8
+    assert saved >= M * 2 * 768 * 2
+    assert fws >= M * (768 + 2048) * 2
+    assert bws >= M * (3 * 768 + 2048) * 2
+    d32 = g.Dims.of(64, 128, 64, 8, 2, "fp32")
+    assert g.workspace_size(d32)[1] >= 128 * 128 * 4
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((0, 128, 64, 8, 2, 1), 2), ((16, 128, 64, 8, 9, 1), 2), ((16, -1, 64, 8, 2, 1), 2),
+    ((16, 100, 64, 8, 2, 1), 3), ((16, 128, 96, 8, 2, 1), 3), ((16, 128, 64, 8, 2, 2), 3),
+    ((16, 128, 64, 1024, 2, 1), 3), ((16, 128, 64, 64, 33, 1), 3), ((16, 128, 64, 8, 2, 7), 3),
+])
+def test_invalid_dims(dims, status):
+    g, lib = _lib()
+    d = g.Dims(*dims)
+    sz = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(d), ctypes.byref(sz), None, None, None) == status
+
+
+class _FakeTensor:
+    """Stands for a device buffer: only its address is used (no launch happens)."""
+
+    def __init__(self, addr, n=1 << 30):
+        self.addr, self.n = addr, n
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+
+def _fake_routing(g, base=0x7F0000000000):
+    f = [_FakeTensor(base + i * 0x100000) for i in range(6)]
+    return g.RoutingBuffers(*f)
+
+
+def test_route_argument_errors_return_before_launch():
+    g, lib = _lib()
+    d = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    r = _fake_routing(g)
+    logits = _FakeTensor(0x7E0000000000)
+    ws = _FakeTensor(0x7D0000000000, 16)          # too small
+    with pytest.raises(g.MoeError) as ei:
+        g.route(d, logits, r, ws, stream=_NullStream())
+    assert ei.value.status == 5
+    with pytest.raises(g.MoeError) as ei:
+        g.route(d, _FakeTensor(0x7E0000000004), r, _FakeTensor(0x7D0000000000), stream=_NullStream())
+    assert ei.value.status == 4                     # misaligned logits
+    bad = _fake_routing(g)
+    bad.gate = None
+    with pytest.raises((g.MoeError, AttributeError)):
+        g.route(d, logits, bad, _FakeTensor(0x7D0000000000), stream=_NullStream())
+    st = lib.moe_route(ctypes.byref(d), None, None, None, 0, None)
+    assert st == 1
+
+
+def test_forward_backward_argument_errors():
+    g, lib = _lib()
+    d = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    r = _fake_routing(g)
+    t = lambda i: _FakeTensor(0x7C0000000000 + i * 0x1000000)
+    with pytest.raises(g.MoeError) as ei:
+        g.forward(d, t(0), t(1), t(2), r, t(3), t(4), _FakeTensor(0x7B0000000000, 255), stream=_NullStream())
+    assert ei.value.status == 5
+    with pytest.raises(g.MoeError) as ei:
+        g.forward(d, t(0), None, t(2), r, t(3), t(4), t(5), stream=_NullStream())
+    assert ei.value.status == 1
+    with pytest.raises(g.MoeError) as ei:
+        g.backward(d, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), t(7), t(8), None,
+                   _FakeTensor(0x7B0000000000, 1), stream=_NullStream())
+    assert ei.value.status == 5
+    with pytest.raises(g.MoeError) as ei:
+        g.backward(d, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), _FakeTensor(0x7C0000000010), t(8), None,
+                   t(9), stream=_NullStream())
+    assert ei.value.status == 4
+    dbad = g.Dims.of(64, 128, 64, 8, 2, "fp8_bwd")
+    with pytest.raises(g.MoeError) as ei:
+        g.forward(dbad, t(0), t(1), t(2), r, t(3), t(4), t(5), stream=_NullStream())
+    assert ei.value.status == 3
+
+
+class _NullStream:
+    cuda_stream = 0
