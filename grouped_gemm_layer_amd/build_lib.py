@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["route.hip", "combine.hip", "gemm_bf16.hip", "gemm_fp32.hip", "api.hip"]
 
 CFLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"),

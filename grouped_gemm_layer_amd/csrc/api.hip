@@ -20,8 +20,8 @@ struct Sizes {
   size_t route_ws, saved, fwd_ws, bwd_ws;
   // carving offsets
   size_t r_partials, r_bases;
-  size_t f_tile_e, f_tile_r, f_A, f_O;
-  size_t b_tile_e, b_tile_r, b_dG13, b_Ag, b_dXp, b_part;
+  size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
+  size_t b_tile_e, b_tile_r, b_tile_x, b_dG13, b_Ag, b_dXp, b_part;
 };
 
 moe_status check_dims(const moe_dims* d) {
@@ -40,7 +40,7 @@ Sizes compute_sizes(const moe_dims* d) {
   const size_t M = (size_t)d->T * d->k;
   const size_t es = (d->mode == MOE_MODE_FP32) ? 4 : 2;
   const bool bf16 = d->mode != MOE_MODE_FP32;
-  const int bm = bf16 ? BF16_BM : FP32_BM;
+  const int bm = row_tile_m(bf16);
   const size_t max_tiles = (size_t)max_row_tiles((int)M, d->E, bm);
   const size_t nblk = (size_t)route_num_blocks((int)M);
   size_t o = 0;
@@ -51,12 +51,14 @@ Sizes compute_sizes(const moe_dims* d) {
   o = 0;
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
+  s.f_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
   s.f_A = o;      o += align_up(M * d->I * es);
   s.f_O = o;      o += align_up(M * d->H * es);
   s.fwd_ws = o;
   o = 0;
   s.b_tile_e = o; o += align_up(max_tiles * 4);
   s.b_tile_r = o; o += align_up(max_tiles * 4);
+  s.b_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
   s.b_dG13 = o;   o += align_up(M * 2 * d->I * es);
   s.b_Ag = o;     o += align_up(M * d->I * es);
   s.b_dXp = o;    o += align_up(M * d->H * es);
@@ -171,10 +173,11 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   a.O = at(ws, s.f_O);
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.f_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.f_tile_r));
-  a.tile_expert = te; a.tile_row0 = tr;
-  const int bm = bf16 ? BF16_BM : FP32_BM;
+  int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.f_tile_x));
+  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
+  const int bm = row_tile_m(bf16);
   hipError_t e = mk.mark();
-  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, stream);
+  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream);
   if (e == hipSuccess) e = mk.mark();
   if (e == hipSuccess) e = gemm(bf16, KIND_FWD1, a, stream);
   if (e == hipSuccess) e = mk.mark();
@@ -216,11 +219,12 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   a.dw2 = dw2;
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.b_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.b_tile_r));
-  a.tile_expert = te; a.tile_row0 = tr;
-  const int bm = bf16 ? BF16_BM : FP32_BM;
+  int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
+  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
+  const int bm = row_tile_m(bf16);
   // activation-gradient chain first; the weight gradients do not feed it
   hipError_t e = mk.mark();
-  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, stream);
+  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream);
   if (e == hipSuccess) e = mk.mark();
   if (e == hipSuccess) e = gemm(bf16, KIND_DGRAD2, a, stream);
   if (e == hipSuccess) e = mk.mark();

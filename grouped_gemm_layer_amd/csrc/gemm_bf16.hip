@@ -10,237 +10,311 @@
 // the dispatch is fused into the operand loads (rows are read from x or dY
 // through the routing map), so the permuted copies are never written.
 //
-// Every kernel computes C[m][n] = sum_k A[m][k] B[n][k] over one 128x128 tile:
+// Every kernel computes C[m][n] = sum_k A[m][k] B[n][k] over one BM x BN tile:
 //   row-ragged kinds (forward, dgrad): m = expert-sorted token rows of one
 //     expert (tile table), n = output features, K = H, I or 2I;
-//   wgrad kinds: m, n = weight-gradient rows/cols of one expert (grid.y),
-//     K = that expert's token rows, ragged and zero-padded.
+//   wgrad kinds: m, n = weight-gradient rows/cols of one expert, K = that
+//     expert's token rows, ragged and zero-padded.
 // Operands come in two global layouts:
-//   KC: element (row, k) at row_ptr(row)[k]        (K contiguous)
-//   KO: element (row, k) at krow_ptr(k)[row]       (rows contiguous, "transposed")
-// Both are staged to LDS as [row][k] (64 k per row, 16-byte chunks XOR
-// swizzled by row) so every MFMA operand is one 16-byte LDS read; KO tiles are
-// transposed in registers (4 k x 8 rows per thread) on the way in.
+//   KC: element (row, k) at row_ptr(row)[k]   (K contiguous)
+//   KO: element (row, k) at krow_ptr(k)[row]  (rows contiguous)
+// KC tiles are stored in LDS as [row][64 k] with 16-byte chunks XOR-swizzled by
+// row and read with ds_read_b128; KO tiles keep their global layout in LDS,
+// [64 k][R rows] with 32-byte granules XOR-swizzled by k, and are read with two
+// ds_read_b64_tr_b16 (gfx950 LDS transpose reads: within each 16-lane group,
+// lane d receives element d%4 of the 8-byte reads of lanes 4j + d/4, j = 0..3).
+// Either way an MFMA operand register holds 8 consecutive k of one row, so the
+// layouts mix freely.
 //
-// Four waves as 2x2, each owning a 64x64 sub-tile = 4x4 MFMA blocks of 16x16.
 // The MFMA's first operand is the B tile (rows n) and its second the A tile
-// (rows m), so lane l holds D[n = 4*(l/16) + v][m = l%16]: four consecutive
+// (rows m): lane l holds D[n = 4*(l/16) + v][m = l%16], i.e. four consecutive
 // output features of one row, stored as one 8- or 16-byte write.
-// Main loop: global loads of tile k+1 into registers overlap the MFMAs of
-// tile k; one barrier per K step (double-buffered LDS).
+//
+// Global loads are raw buffer loads (16 bytes per lane): an offset past the
+// buffer's end returns zeros, which pads the ragged K tail of the wgrad GEMMs
+// without branches.  Pipeline: global -> registers two K tiles ahead (two
+// register sets), LDS double buffer, one barrier per K tile; the token offsets
+// of the gathered wgrad rows come from an LDS table refilled every 2048 rows.
+// Blocks are renumbered so that each XCD (8 per chip, blocks dealt
+// round-robin) receives a contiguous range of the expert-major tile order and
+// its L2 serves the shared weight and token panels.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = BF16_BM;   // 128
-constexpr int BN = BF16_BN;   // 128
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+
 constexpr int BK = 64;
-constexpr int NTHR = 256;
-constexpr int WM = BM / 2, WN = BN / 2;
-constexpr int FM = WM / 16, FN = WN / 16;
-static_assert(BM == 128 && BN == 128, "loaders assume 128-row tiles");
+constexpr int NXCD = 8;
+constexpr int TOKTAB = 2048;                 // gathered K rows per LDS token table
+constexpr uint32_t OOB = 0x80000000u;        // buffer offset that reads as zeros
 
-// element offset of (row, 8-element chunk) inside a [rows][BK] LDS tile
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
-}
-
-template <int KIND> struct KindTraits;
-// A = gathered x rows (KC), B = W13 rows (KC, G1/G3 paired), K = H
-template <> struct KindTraits<KIND_FWD1> { static constexpr bool ragged_rows = true, a_ko = false, b_ko = false; };
-// A = A rows (KC), B = W2 rows (KC), K = I
-template <> struct KindTraits<KIND_FWD2> { static constexpr bool ragged_rows = true, a_ko = false, b_ko = false; };
-// A = gathered dY rows (KC), B[n=i][k=h] = W2[h][i] (KO), K = H
-template <> struct KindTraits<KIND_DGRAD2> { static constexpr bool ragged_rows = true, a_ko = false, b_ko = true; };
-// A = dG13 rows (KC), B[n=h][k=j] = W13[j][h] (KO), K = 2I
-template <> struct KindTraits<KIND_DGRAD1> { static constexpr bool ragged_rows = true, a_ko = false, b_ko = true; };
-// A[m=h][k=r] = dY[t(r)][h] (KO), B[n=i][k=r] = Ag[r][i] (KO)
-template <> struct KindTraits<KIND_WGRAD2> { static constexpr bool ragged_rows = false, a_ko = true, b_ko = true; };
-// A[m=j][k=r] = dG13[r][j] (KO), B[n=h][k=r] = x[t(r)][h] (KO)
-template <> struct KindTraits<KIND_WGRAD1> { static constexpr bool ragged_rows = false, a_ko = true, b_ko = true; };
-
-// KC loader: 128 rows x 64 k; thread handles rows (tid>>3) + 32*i, chunk tid&7.
-struct KcLoader {
-  const bf16_t* p[4];   // row base (already offset by chunk), nullptr = zero row
-  uint4 r[4];
-  __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (p[i]) r[i] = *reinterpret_cast<const uint4*>(p[i] + kt * BK);
-      else r[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(lds + lds_off(row, tid & 7)) = r[i];
-    }
-  }
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int WPE = WPE_;   // waves per SIMD the register allocation must allow
+  // blocks resident on one XCD at a time (32 CUs, WPE waves per SIMD): the
+  // size of the tile groups that should share operands
+  static constexpr int GROUP = 32 * (4 * WPE) / (WGM_ * WGN_);
+  static constexpr int NTHR = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
 };
 
-// KO loader: 64 k x 128 rows; thread handles k = 4q..4q+3 (q = tid>>4) and
-// rows 8c..8c+7 (c = tid&15).  Transposed to [row][k] on the LDS store.
-struct KoLoader {
-  uint4 r[4];
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-    const int q = tid >> 4, c = tid & 15;
-    const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-    const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
-    const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
-    const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = j >> 1;
-      uint32_t lo, hi;
-      if (j & 1) {
-        lo = (w0[d] >> 16) | (w1[d] & 0xFFFF0000u);
-        hi = (w2[d] >> 16) | (w3[d] & 0xFFFF0000u);
-      } else {
-        lo = (w0[d] & 0xFFFFu) | (w1[d] << 16);
-        hi = (w2[d] & 0xFFFFu) | (w3[d] << 16);
-      }
-      const int row = 8 * c + j;
-      *reinterpret_cast<uint2*>(lds + lds_off(row, q >> 1) + 4 * (q & 1)) = make_uint2(lo, hi);
-    }
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// ---- LDS layouts (element offsets) ----
+// KC: [row][64], 16-byte chunk c of row r stored at chunk c ^ ((r ^ r>>3) & 7)
+__device__ __forceinline__ int kc_off(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+// KO: [64 k][R], 32-byte granule g of k-row k stored at granule g ^ f(k);
+// f spreads the 16 k-rows one transpose read touches over distinct granules.
+template <int R>
+__device__ __forceinline__ int ko_f(int k) {
+  if constexpr (R >= 256) return (k & 3) | (((k >> 3) & 3) << 2);
+  else if constexpr (R == 128) return (k & 3) | (((k >> 3) & 1) << 2);
+  else return k & 3;
+}
+template <int R>
+__device__ __forceinline__ int ko_off(int k, int col) {
+  return k * R + ((((col >> 4) ^ ko_f<R>(k)) << 4) | (col & 15));
+}
+
+// MFMA operand fragment: 16 rows starting at `row0`, k = 32*ks + 8*(lane/16) + 0..7
+__device__ __forceinline__ bf16x8_t frag_kc(const bf16_t* lds, int row0, int ks, int lane) {
+  return *reinterpret_cast<const bf16x8_t*>(lds + kc_off(row0 + (lane & 15), ks * 4 + (lane >> 4)));
+}
+template <int R>
+__device__ __forceinline__ bf16x8_t frag_ko(const bf16_t* lds, int row0, int ks, int lane) {
+  const int s = lane & 15;
+  const int k = ks * 32 + 8 * (lane >> 4) + (s >> 2);
+  const int col = row0 + 4 * (s & 3);
+  const bf16_t* p0 = lds + ko_off<R>(k, col);
+  const bf16_t* p1 = lds + ko_off<R>(k + 4, col);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p0));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---- per-kind operand description ----
+template <int KIND> struct Kind;
+template <> struct Kind<KIND_FWD1> {   // A = x[tok(r)] (KC), B = W13 rows, G1/G3 paired (KC); K = H
+  static constexpr bool ragged_rows = true, a_ko = false, b_ko = false, a_gk = false, b_gk = false;
+};
+template <> struct Kind<KIND_FWD2> {   // A = A rows (KC), B = W2 rows (KC); K = I
+  static constexpr bool ragged_rows = true, a_ko = false, b_ko = false, a_gk = false, b_gk = false;
+};
+template <> struct Kind<KIND_DGRAD2> { // A = dY[tok(r)] (KC), B[n=i][k=h] = W2[h][i] (KO); K = H
+  static constexpr bool ragged_rows = true, a_ko = false, b_ko = true, a_gk = false, b_gk = false;
+};
+template <> struct Kind<KIND_DGRAD1> { // A = dG13 rows (KC), B[n=h][k=j] = W13[j][h] (KO); K = 2I
+  static constexpr bool ragged_rows = true, a_ko = false, b_ko = true, a_gk = false, b_gk = false;
+};
+template <> struct Kind<KIND_WGRAD2> { // A[m=h][k=r] = dY[tok(r)][h] (KO, gathered), B[n=i][k=r] = Ag[r][i] (KO)
+  static constexpr bool ragged_rows = false, a_ko = true, b_ko = true, a_gk = true, b_gk = false;
+};
+template <> struct Kind<KIND_WGRAD1> { // A[m=j][k=r] = dG13[r][j] (KO), B[n=h][k=r] = x[tok(r)][h] (KO, gathered)
+  static constexpr bool ragged_rows = false, a_ko = true, b_ko = true, a_gk = false, b_gk = true;
 };
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-template <int KIND>
-__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(LayerArgs a, int n_tiles) {
-  using Tr = KindTraits<KIND>;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
-  // after the main loop's last barrier the A tiles are free: reused for the
-  // gate-gradient reduction of the dgrad epilogue
-  float* s_part = reinterpret_cast<float*>(&sA[0][0]);
+template <int KIND, class C>
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::WPE)))
+void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
+  using K_ = Kind<KIND>;
+  constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int CHA = BM * BK / 8 / NTHR;   // 16-byte chunks per thread per K tile
+  constexpr int CHB = BN * BK / 8 / NTHR;
+  constexpr bool gathered_k = K_::a_gk || K_::b_gk;
+  static_assert(CHA >= 1 && CHB >= 1, "tile too small for the thread count");
+
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
+  bf16_t (*sA)[BM * BK] = reinterpret_cast<bf16_t (*)[BM * BK]>(smem);              // [2][BM*BK]
+  bf16_t (*sB)[BN * BK] = reinterpret_cast<bf16_t (*)[BN * BK]>(smem + 2 * BM * BK);  // [2][BN*BK]
+  __shared__ uint32_t s_tok[gathered_k ? TOKTAB : 1];   // element offset of each gathered row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---------------- tile decode ----------------
+  // ---------------- tile decode (XCD-contiguous renumbering) ----------------
+  const int per_xcd = gridDim.x / NXCD;
+  const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  if (L >= tiles_total) return;
   int e, m0, mlim, n0, klo = 0, khi = 0, nk;
-  if constexpr (Tr::ragged_rows) {
-    const int nt = blockIdx.x % n_tiles;
-    const int mt = blockIdx.x / n_tiles;
-    e = a.tile_expert[mt];
+  if constexpr (K_::ragged_rows) {
+    // Logical order: expert-major; inside an expert, groups of gn column
+    // tiles, and inside a group all of the expert's row tiles with the gn
+    // columns fastest, so that about one XCD's worth of concurrent blocks
+    // shares the same token rows and weight rows.
+    e = a.tile_expert[L / n_tiles];
     if (e < 0) return;
-    m0 = a.tile_row0[mt];
+    const int t0 = a.expert_tile0[e];
+    const int me = a.expert_tile0[e + 1] - t0;            // row tiles of this expert
+    const int local = L - t0 * n_tiles;
+    const int gn = max(1, min(n_tiles, C::GROUP / me));
+    const int ng = local / (me * gn);
+    const int gs = min(gn, n_tiles - ng * gn);
+    const int rem = local - ng * me * gn;
+    const int nt = ng * gn + rem % gs;
+    m0 = a.tile_row0[t0 + rem / gs];
     mlim = a.offsets[e + 1];
     n0 = nt * (KIND == KIND_FWD1 ? BN / 2 : BN);
-    const int K = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) ? H : (KIND == KIND_FWD2 ? I : 2 * I);
-    nk = K / BK;
+    const int Kd = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) ? H : (KIND == KIND_FWD2 ? I : 2 * I);
+    nk = Kd / BK;
   } else {
-    e = blockIdx.y;
-    const int nt = blockIdx.x % n_tiles;
-    const int mt = blockIdx.x / n_tiles;
-    m0 = mt * BM;
-    n0 = nt * BN;
+    const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
+    e = L / per_e;
+    const int t = L % per_e;
+    m0 = (t / n_tiles) * BM;
+    n0 = (t % n_tiles) * BN;
     klo = a.offsets[e];
     khi = a.offsets[e + 1];
     nk = (khi - klo + BK - 1) / BK;
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
-  // valid extent along n
-  const int nlim = (KIND == KIND_FWD1) ? I
-                 : (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) ? H
-                 : (KIND == KIND_DGRAD2) ? I
-                 : (KIND == KIND_WGRAD2) ? I : H;
+  const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
 
-  const bf16_t* x = static_cast<const bf16_t*>(a.x);
-  const bf16_t* dy = static_cast<const bf16_t*>(a.dy);
-  const bf16_t* w13 = static_cast<const bf16_t*>(a.w13) + (size_t)e * 2 * I * H;
-  const bf16_t* w2 = static_cast<const bf16_t*>(a.w2) + (size_t)e * H * I;
-
-  // ---------------- operand setup ----------------
-  KcLoader la{}, lb{};
-  KoLoader oa{}, ob{};
-  if constexpr (!Tr::a_ko) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + (tid >> 3) + 32 * i;
-      const bf16_t* p = nullptr;
-      if (row < mlim) {
-        if constexpr (KIND == KIND_FWD1) p = x + (size_t)(a.s2f[row] / k) * H;
-        else if constexpr (KIND == KIND_DGRAD2) p = dy + (size_t)(a.s2f[row] / k) * H;
-        else if constexpr (KIND == KIND_FWD2) p = static_cast<const bf16_t*>(a.A) + (size_t)row * I;
-        else p = static_cast<const bf16_t*>(a.dG13) + (size_t)row * 2 * I;
-        p += (tid & 7) * 8;
-      }
-      la.p[i] = p;
-    }
+  // ---------------- buffer resources ----------------
+  const size_t M = (size_t)a.M;
+  __amdgpu_buffer_rsrc_t ra_src, rb_src;
+  if constexpr (KIND == KIND_FWD1) {
+    ra_src = make_rsrc(a.x, (uint32_t)((size_t)a.T * H * 2));
+    rb_src = make_rsrc(static_cast<const bf16_t*>(a.w13) + (size_t)e * 2 * I * H, (uint32_t)((size_t)2 * I * H * 2));
+  } else if constexpr (KIND == KIND_FWD2) {
+    ra_src = make_rsrc(a.A, (uint32_t)(M * I * 2));
+    rb_src = make_rsrc(static_cast<const bf16_t*>(a.w2) + (size_t)e * H * I, (uint32_t)((size_t)H * I * 2));
+  } else if constexpr (KIND == KIND_DGRAD2) {
+    ra_src = make_rsrc(a.dy, (uint32_t)((size_t)a.T * H * 2));
+    rb_src = make_rsrc(static_cast<const bf16_t*>(a.w2) + (size_t)e * H * I, (uint32_t)((size_t)H * I * 2));
+  } else if constexpr (KIND == KIND_DGRAD1) {
+    ra_src = make_rsrc(a.dG13, (uint32_t)(M * 2 * I * 2));
+    rb_src = make_rsrc(static_cast<const bf16_t*>(a.w13) + (size_t)e * 2 * I * H, (uint32_t)((size_t)2 * I * H * 2));
+  } else if constexpr (KIND == KIND_WGRAD2) {
+    ra_src = make_rsrc(a.dy, (uint32_t)((size_t)a.T * H * 2));
+    rb_src = make_rsrc(a.Ag, (uint32_t)(M * I * 2));
+  } else {
+    ra_src = make_rsrc(a.dG13, (uint32_t)(M * 2 * I * 2));
+    rb_src = make_rsrc(a.x, (uint32_t)((size_t)a.T * H * 2));
   }
-  if constexpr (!Tr::b_ko) {
+
+  // ---------------- per-thread operand offsets (bytes) ----------------
+  // KC: chunk i of the thread = row (q >> 3), 16-byte column chunk (q & 7), q = tid + NTHR*i
+  // KO: chunk i of the thread = k-row q / (R/8), columns 8*(q % (R/8))
+  // KC operands: byte offset of each chunk's row start (fixed for the block).
+  // KO operands: the column offset is the same for all chunks of a thread
+  // (NTHR is a multiple of R/8); chunk i covers k-row tid/(R/8) + i*NTHR/(R/8).
+  uint32_t oa[K_::a_ko ? 1 : CHA], ob[K_::b_ko ? 1 : CHB];
+  if constexpr (!K_::a_ko) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nn = (tid >> 3) + 32 * i;
-      const bf16_t* p = nullptr;
+    for (int i = 0; i < CHA; ++i) {
+      const int q = tid + NTHR * i;
+      const int row = min(m0 + (q >> 3), mlim - 1);   // rows past the segment: any valid row
+      uint32_t o;
+      if constexpr (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) o = (uint32_t)(a.s2f[row] / k) * H;
+      else if constexpr (KIND == KIND_FWD2) o = (uint32_t)row * I;
+      else o = (uint32_t)row * 2 * I;
+      oa[i] = (o + (q & 7) * 8) * 2;
+    }
+  } else {
+    oa[0] = min(m0 + 8 * (tid % (BM / 8)), mlim - 8) * 2;
+  }
+  if constexpr (!K_::b_ko) {
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) {
+      const int q = tid + NTHR * i;
+      const int nn = q >> 3;
+      uint32_t o;
       if constexpr (KIND == KIND_FWD1) {
-        const int c = n0 + (nn & (BN / 2 - 1));
-        if (c < I) p = w13 + (size_t)((nn < BN / 2) ? c : I + c) * H;
-      } else {  // FWD2
-        const int n = n0 + nn;
-        if (n < H) p = w2 + (size_t)n * I;
-      }
-      if (p) p += (tid & 7) * 8;
-      lb.p[i] = p;
-    }
-  }
-  // KO loads: k rows kbase + 4q + i, columns col0 + 8c
-  const int q = tid >> 4, c8 = (tid & 15) * 8;
-  auto load_ko_a = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = klo + kt * BK + 4 * q + i;
-      const int col = m0 + c8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < khi && col < mlim) {
-        const bf16_t* p;
-        if constexpr (KIND == KIND_WGRAD2) p = dy + (size_t)(a.s2f[r] / k) * H + col;
-        else p = static_cast<const bf16_t*>(a.dG13) + (size_t)r * 2 * I + col;
-        v = *reinterpret_cast<const uint4*>(p);
-      }
-      oa.r[i] = v;
-    }
-  };
-  auto load_ko_b = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = n0 + c8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if constexpr (Tr::ragged_rows) {   // dense K of the weights
-        const int kr = kt * BK + 4 * q + i;
-        if (col < nlim) {
-          const bf16_t* p;
-          if constexpr (KIND == KIND_DGRAD2) p = w2 + (size_t)kr * I + col;
-          else p = w13 + (size_t)kr * H + col;
-          v = *reinterpret_cast<const uint4*>(p);
-        }
+        const int c = min(n0 + (nn & (BN / 2 - 1)), I - 1);
+        o = (uint32_t)((nn < BN / 2) ? c : I + c) * H;
       } else {
-        const int r = klo + kt * BK + 4 * q + i;
-        if (r < khi && col < nlim) {
-          const bf16_t* p;
-          if constexpr (KIND == KIND_WGRAD2) p = static_cast<const bf16_t*>(a.Ag) + (size_t)r * I + col;
-          else p = x + (size_t)(a.s2f[r] / k) * H + col;
-          v = *reinterpret_cast<const uint4*>(p);
-        }
+        o = (uint32_t)min(n0 + nn, H - 1) * I;
       }
-      ob.r[i] = v;
+      ob[i] = (o + (q & 7) * 8) * 2;
+    }
+  } else {
+    ob[0] = min(n0 + 8 * (tid % (BN / 8)), nlim - 8) * 2;
+  }
+  static_assert(NTHR % (BM / 8) == 0 && NTHR % (BN / 8) == 0, "KO chunk columns must be per-thread constants");
+  const int krow_a0 = tid / (BM / 8), krow_b0 = tid / (BN / 8);
+  auto krow_a = [&](int i) { return krow_a0 + i * (NTHR / (BM / 8)); };
+  auto krow_b = [&](int i) { return krow_b0 + i * (NTHR / (BN / 8)); };
+
+  // byte offset of operand chunk i for K tile kt (kt may run past nk: the
+  // wgrad rows then read as zeros, the dense-K kinds re-read the last tile)
+  auto a_off = [&](int i, int kt) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!K_::a_ko) {
+      return oa[i] + (uint32_t)min(kt, nk - 1) * (BK * 2);
+    } else {
+      const int rr = kt * BK + krow_a(i);
+      if constexpr (KIND == KIND_WGRAD2) {   // dY rows of the gathered tokens
+        const uint32_t t = s_tok[rr & (TOKTAB - 1)];
+        return (klo + rr < khi) ? t * 2 + oa[0] : OOB;
+      } else {                               // dG13 rows
+        return (klo + rr < khi) ? (uint32_t)(klo + rr) * (2 * I * 2) + oa[0] : OOB;
+      }
     }
   };
-  auto load_tile = [&](int kt) {
-    if constexpr (Tr::a_ko) load_ko_a(kt); else la.load(kt);
-    if constexpr (Tr::b_ko) load_ko_b(kt); else lb.load(kt);
+  auto b_off = [&](int i, int kt) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!K_::b_ko) {
+      return ob[i] + (uint32_t)min(kt, nk - 1) * (BK * 2);
+    } else if constexpr (K_::ragged_rows) {   // weights, dense K rows
+      const int kr = min(kt, nk - 1) * BK + krow_b(i);
+      return (uint32_t)kr * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + ob[0];
+    } else {
+      const int rr = kt * BK + krow_b(i);
+      if constexpr (KIND == KIND_WGRAD2) {   // Ag rows
+        return (klo + rr < khi) ? (uint32_t)(klo + rr) * (I * 2) + ob[0] : OOB;
+      } else {                               // x rows of the gathered tokens
+        const uint32_t t = s_tok[rr & (TOKTAB - 1)];
+        return (klo + rr < khi) ? t * 2 + ob[0] : OOB;
+      }
+    }
   };
-  auto store_tile = [&](int buf) {
-    if constexpr (Tr::a_ko) oa.store(sA[buf], tid); else la.store(sA[buf], tid);
-    if constexpr (Tr::b_ko) ob.store(sB[buf], tid); else lb.store(sB[buf], tid);
+
+  // token offsets of gathered rows [klo + base, klo + base + TOKTAB)
+  auto fill_tok = [&](int base) {
+    for (int j = tid; j < TOKTAB; j += NTHR) {
+      const int r = min(klo + base + j, khi - 1);
+      s_tok[j] = (uint32_t)(a.s2f[r] / k) * H;
+    }
+  };
+
+  u32x4_t ra0[CHA], rb0[CHB], ra1[CHA], rb1[CHB];
+
+  auto load_tile = [&](u32x4_t (&ra)[CHA], u32x4_t (&rb)[CHB], int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CHA; ++i) ra[i] = bload(ra_src, a_off(i, kt));
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) rb[i] = bload(rb_src, b_off(i, kt));
+  };
+  auto store_tile = [&](const u32x4_t (&ra)[CHA], const u32x4_t (&rb)[CHB], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CHA; ++i) {
+      const int q = tid + NTHR * i;
+      const int off = K_::a_ko ? ko_off<BM>(krow_a(i), 8 * (tid % (BM / 8))) : kc_off(q >> 3, q & 7);
+      *reinterpret_cast<u32x4_t*>(&sA[buf][off]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) {
+      const int q = tid + NTHR * i;
+      const int off = K_::b_ko ? ko_off<BN>(krow_b(i), 8 * (tid % (BN / 8))) : kc_off(q >> 3, q & 7);
+      *reinterpret_cast<u32x4_t*>(&sB[buf][off]) = rb[i];
+    }
   };
 
   // LDS row of the j-th 16-row MFMA block of this wave's B sub-tile
@@ -258,33 +332,55 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(LayerArgs a, int n_tile
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
+  auto compute = [&](int buf) __attribute__((always_inline)) {
     const bf16_t* As = sA[buf];
     const bf16_t* Bs = sB[buf];
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      const int chunk = ks * 4 + (lane >> 4);
       bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * WM + 16 * i + (lane & 15), chunk));
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (K_::a_ko) af[i] = frag_ko<BM>(As, wm * WM + 16 * i, ks, lane);
+        else af[i] = frag_kc(As, wm * WM + 16 * i, ks, lane);
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(brow(j) + (lane & 15), chunk));
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (K_::b_ko) bfr[j] = frag_ko<BN>(Bs, brow(j), ks, lane);
+        else bfr[j] = frag_kc(Bs, brow(j), ks, lane);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+  };
+
+  // ---------------- main loop ----------------
+  // tile kt is in LDS buffer kt&1 while tiles kt+1 and kt+2 are in registers
+  if (nk > 0) {
+    if constexpr (gathered_k) { fill_tok(0); __syncthreads(); }
+    load_tile(ra0, rb0, 0);
+    load_tile(ra1, rb1, 1);
+    store_tile(ra0, rb0, 0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; kt += 2) {
+    if constexpr (gathered_k) {
+      // the next loads reach row kt+2's table chunk: refill after everyone is done with the old one
+      if (((kt + 2) * BK) % TOKTAB == 0 && kt + 2 < nk) {
+        fill_tok((kt + 2) * BK);
+        __syncthreads();
+      }
+    }
+    load_tile(ra0, rb0, kt + 2);
+    compute(0);
+    store_tile(ra1, rb1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    load_tile(ra1, rb1, kt + 3);
+    compute(1);
+    store_tile(ra0, rb0, 0);
     __syncthreads();
   }
 
@@ -330,6 +426,9 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(LayerArgs a, int n_tile
     const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
     bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
     bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
+    // after the main loop's last barrier the A tiles are free: reused for the
+    // cross-wave reduction of the gate-gradient partials
+    float* s_part = reinterpret_cast<float*>(smem);
     float psum[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -365,82 +464,96 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(LayerArgs a, int n_tile
         *reinterpret_cast<uint2*>(Ag + (size_t)m * I + n) = pack4(ag[0], ag[1], ag[2], ag[3]);
       }
     }
-    // reduce the gate-gradient partial over this tile's n: lanes sharing a row,
-    // then the two waves of a row block (fixed order: deterministic)
+    // lanes sharing a row, then the WGN waves of a row block, in a fixed order
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       psum[i] += __shfl_xor(psum[i], 16);
       psum[i] += __shfl_xor(psum[i], 32);
     }
-    if (wn == 1 && lane < 16) {
+    if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) s_part[wm * WM + 16 * i + lane] = psum[i];
+      for (int i = 0; i < FM; ++i) s_part[wn * BM + wm * WM + 16 * i + lane] = psum[i];
     }
     __syncthreads();
-    if (wn == 0 && lane < 16) {
-      const int nt = n0 / BN;
+    for (int ml = tid; ml < BM; ml += NTHR) {
+      const int m = m0 + ml;
+      if (m < mlim) {
+        float p = 0.f;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int ml = wm * WM + 16 * i + lane;
-        const int m = m0 + ml;
-        if (m < mlim) a.dgate_part[(size_t)nt * a.M + m] = psum[i] + s_part[ml];
+        for (int w = 0; w < C::WGN; ++w) p += s_part[w * BM + ml];
+        a.dgate_part[(size_t)(n0 / BN) * a.M + m] = p;
       }
     }
-  } else {   // wgrad: fp32 output of one expert
-    float* out = (KIND == KIND_WGRAD2) ? a.dw2 + (size_t)e * H * I : a.dw13 + (size_t)e * 2 * I * H;
-    const int ld = (KIND == KIND_WGRAD2) ? I : H;
+  } else {   // wgrad: fp32 output of one expert, staged through LDS so each
+             // store instruction writes whole rows (full cache lines)
+    static_assert(BM * BN * 4 <= 2 * (BM + BN) * BK * 2, "fp32 tile must fit in the operand LDS");
+    float* s_out = reinterpret_cast<float*>(smem);
+    constexpr int NQ = BN / 4;                             // 16-byte chunks per row
+    auto out_off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ)) << 2); };
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WM + 16 * i + mrow;
-      if (m >= mlim) continue;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * WN + 16 * j + ncol;
-        if (n >= nlim) continue;
-        const f32x4_t v = acc[i][j];
-        *reinterpret_cast<float4*>(out + (size_t)m * ld + n) = make_float4(v[0], v[1], v[2], v[3]);
+        const int row = wm * WM + 16 * i + mrow;
+        const int q = (wn * WN + 16 * j + ncol) >> 2;
+        *reinterpret_cast<f32x4_t*>(&s_out[out_off(row, q)]) = acc[i][j];
       }
+    __syncthreads();
+    float* out = (KIND == KIND_WGRAD2) ? a.dw2 + (size_t)e * H * I : a.dw13 + (size_t)e * 2 * I * H;
+    const int ld = (KIND == KIND_WGRAD2) ? I : H;
+    for (int c = tid; c < BM * NQ; c += NTHR) {
+      const int row = c / NQ, q = c % NQ;
+      const int m = m0 + row, n = n0 + 4 * q;
+      if (m < mlim && n < nlim)
+        *reinterpret_cast<f32x4_t*>(out + (size_t)m * ld + n) = *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]);
     }
   }
 }
 
+// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD).
+#ifndef MOE_CFG_ROW
+#define MOE_CFG_ROW 128, 128, 2, 2, 2
+#endif
+#ifndef MOE_CFG_WGRAD
+#define MOE_CFG_WGRAD 128, 128, 2, 2, 1
+#endif
+using CfgRow = TileCfg<MOE_CFG_ROW>;
+using CfgW = TileCfg<MOE_CFG_WGRAD>;
+
+template <int KIND, class C>
+hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
+  int n_tiles, tiles;
+  if constexpr (Kind<KIND>::ragged_rows) {
+    const int ncols = (KIND == KIND_FWD1) ? a.I : (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) ? a.H : a.I;
+    const int bn = (KIND == KIND_FWD1) ? C::BN / 2 : C::BN;
+    n_tiles = (ncols + bn - 1) / bn;
+    tiles = n_tiles * max_row_tiles(a.M, a.E, C::BM);
+  } else {
+    const int mdim = (KIND == KIND_WGRAD2) ? a.H : 2 * a.I;
+    const int ndim = (KIND == KIND_WGRAD2) ? a.I : a.H;
+    n_tiles = (ndim + C::BN - 1) / C::BN;
+    tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
+  }
+  const int grid = (tiles + NXCD - 1) / NXCD * NXCD;
+  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, n_tiles, tiles);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+int bf16_row_tile_m() { return CfgRow::BM; }
+int bf16_dgrad2_tile_n() { return CfgRow::BN; }
+
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s) {
-  const int max_mt = max_row_tiles(a.M, a.E, BM);
   switch (kind) {
-    case KIND_FWD1: {
-      const int nt = (a.I + BN / 2 - 1) / (BN / 2);
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_FWD1>, dim3(nt * max_mt), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
-    case KIND_FWD2: {
-      const int nt = (a.H + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_FWD2>, dim3(nt * max_mt), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
-    case KIND_DGRAD2: {
-      const int nt = (a.I + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_DGRAD2>, dim3(nt * max_mt), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
-    case KIND_DGRAD1: {
-      const int nt = (a.H + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_DGRAD1>, dim3(nt * max_mt), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
-    case KIND_WGRAD2: {
-      const int nt = (a.I + BN - 1) / BN, mt = (a.H + BM - 1) / BM;
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_WGRAD2>, dim3(nt * mt, a.E), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
-    case KIND_WGRAD1: {
-      const int nt = (a.H + BN - 1) / BN, mt = (2 * a.I + BM - 1) / BM;
-      hipLaunchKernelGGL(gemm_bf16_kernel<KIND_WGRAD1>, dim3(nt * mt, a.E), dim3(NTHR), 0, s, a, nt);
-      break;
-    }
+    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRow>(a, s);
+    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRow>(a, s);
+    case KIND_DGRAD2: return launch_kind<KIND_DGRAD2, CfgRow>(a, s);
+    case KIND_DGRAD1: return launch_kind<KIND_DGRAD1, CfgRow>(a, s);
+    case KIND_WGRAD2: return launch_kind<KIND_WGRAD2, CfgW>(a, s);
+    case KIND_WGRAD1: return launch_kind<KIND_WGRAD1, CfgW>(a, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -59,6 +59,7 @@ struct LayerArgs {
   // tile table for row-ragged GEMMs (device, written by build_tile_table)
   const int32_t* tile_expert;     // [max_tiles]
   const int32_t* tile_row0;       // [max_tiles]
+  const int32_t* expert_tile0;    // [E+1] first row tile of each expert
   // inputs
   const void* x;                  // [T,H]
   const void* w13;                // [E,2I,H]
@@ -100,7 +101,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 int route_num_blocks(int M);   // blocks of the histogram / scatter passes
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles,
-                             int32_t* tile_expert, int32_t* tile_row0, hipStream_t s);
+                             int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, hipStream_t s);
 
 // combine / unpermute-reduce (fp32 accumulate in slot order)
 template <typename T>
@@ -115,14 +116,16 @@ hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s);
 hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s);
 
-// tiling constants the API layer needs for workspace sizing
-constexpr int BF16_BM = 128;     // rows (tokens) per tile of the row-ragged bf16 GEMMs
-constexpr int BF16_BN = 128;
+// tiling the API layer needs for workspace sizing and the tile table
+int bf16_row_tile_m();      // token rows per tile of the row-ragged bf16 GEMMs
+int bf16_dgrad2_tile_n();   // columns per tile of the bf16 dgrad of W2
 constexpr int FP32_BM = 64;
 constexpr int FP32_BN = 64;
+inline int row_tile_m(bool bf16) { return bf16 ? bf16_row_tile_m() : FP32_BM; }
 inline int dgrad2_parts(bool bf16, int I) {
-  // N tiles of the dgrad of W2 (N = I): one partial per tile for the gate gradient
-  return bf16 ? (I + BF16_BN - 1) / BF16_BN : (I + FP32_BN - 1) / FP32_BN;
+  // N tiles of the dgrad of W2 (N = I): one gate-gradient partial per tile
+  const int bn = bf16 ? bf16_dgrad2_tile_n() : FP32_BN;
+  return (I + bn - 1) / bn;
 }
 
 }  // namespace moe

@@ -186,9 +186,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 
 // Tile table of the row-ragged GEMMs: tile i covers rows [row0, row0 + bm) of
 // expert tile_expert[i] (clipped to the expert's end); unused tiles get -1.
+// expert_tile0[e] = first tile of expert e (expert_tile0[E] = number of tiles).
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                           int max_tiles, int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ tile_row0) {
+                                                          int32_t* __restrict__ tile_row0,
+                                                          int32_t* __restrict__ expert_tile0) {
   __shared__ int s_start[2][MAX_E + 1];
   const int e = threadIdx.x;
   int cur = 0;
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   }
   // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
   const int total = s_start[cur][E - 1];
+  if (e <= E) expert_tile0[e] = (e == 0) ? 0 : s_start[cur][e - 1];
   for (int t = threadIdx.x; t < max_tiles; t += 1024) {
     int ex = -1, r0 = 0;
     if (t < total) {
@@ -225,9 +228,9 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 }
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles, int32_t* tile_expert,
-                             int32_t* tile_row0, hipStream_t s) {
+                             int32_t* tile_row0, int32_t* expert_tile0, hipStream_t s) {
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
-                     tile_row0);
+                     tile_row0, expert_tile0);
   return hipGetLastError();
 }
 
