@@ -52,17 +52,21 @@ constexpr int NXCD = 8;
 constexpr int TOKTAB = 2048;                 // gathered K rows per LDS token table
 constexpr uint32_t OOB = 0x80000000u;        // buffer offset that reads as zeros
 
-template <int BM_, int BN_, int WGM_, int WGN_, int WPE_>
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int WPE = WPE_;   // waves per SIMD the register allocation must allow
-  // blocks resident on one XCD at a time (32 CUs, WPE waves per SIMD): the
-  // size of the tile groups that should share operands
-  static constexpr int GROUP = 32 * (4 * WPE) / (WGM_ * WGN_);
-  static constexpr int NTHR = 64 * WGM * WGN;
+  static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
+  static constexpr int STAGES = ST_;    // LDS stages in flight (>= 2)
+  static constexpr int NW = WGM * WGN, NTHR = 64 * NW;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 16, FN = WN / 16;
+  // 1 KiB LDS DMA instructions per wave per K tile, A and B operands
+  static constexpr int DA = BM * BK * 2 / 1024 / NW, DB = BN * BK * 2 / 1024 / NW;
+  // blocks resident on one XCD at a time: the size of the tile groups that share operands
+  static constexpr int GROUP = 32 * (4 * WPE) / NW;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(DA * NW * 1024 == BM * BK * 2 && DB * NW * 1024 == BN * BK * 2, "tiles must split into 1 KiB DMA rows");
+  static_assert(STAGES >= 2, "need at least two LDS stages");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -71,6 +75,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
+
+// 16-byte buffer load straight into LDS: lane l writes LDS bytes [m0 + 16 l, +16).
+// Issued as inline assembly so that the compiler neither tracks nor waits on
+// it; completion is awaited explicitly (vm_wait) before the barrier that
+// publishes a stage.  An offset past the buffer's end stores zeros.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t lds_m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(byte_off), "s"(r), "s"(lds_m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 // ---- LDS layouts (element offsets) ----
 // KC: [row][64], 16-byte chunk c of row r stored at chunk c ^ ((r ^ r>>3) & 7)
@@ -136,14 +154,11 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::WPE)
 void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   using K_ = Kind<KIND>;
   constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
-  constexpr int CHA = BM * BK / 8 / NTHR;   // 16-byte chunks per thread per K tile
-  constexpr int CHB = BN * BK / 8 / NTHR;
+  constexpr int DA = C::DA, DB = C::DB, NW = C::NW;
   constexpr bool gathered_k = K_::a_gk || K_::b_gk;
-  static_assert(CHA >= 1 && CHB >= 1, "tile too small for the thread count");
 
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
-  bf16_t (*sA)[BM * BK] = reinterpret_cast<bf16_t (*)[BM * BK]>(smem);              // [2][BM*BK]
-  bf16_t (*sB)[BN * BK] = reinterpret_cast<bf16_t (*)[BN * BK]>(smem + 2 * BM * BK);  // [2][BN*BK]
+  constexpr int S = C::STAGES, STAGE = (BM + BN) * BK;   // elements per stage: A tile then B tile
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[S * STAGE];
   __shared__ uint32_t s_tok[gathered_k ? TOKTAB : 1];   // element offset of each gathered row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -211,80 +226,58 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     rb_src = make_rsrc(a.x, (uint32_t)((size_t)a.T * H * 2));
   }
 
-  // ---------------- per-thread operand offsets (bytes) ----------------
-  // KC: chunk i of the thread = row (q >> 3), 16-byte column chunk (q & 7), q = tid + NTHR*i
-  // KO: chunk i of the thread = k-row q / (R/8), columns 8*(q % (R/8))
-  // KC operands: byte offset of each chunk's row start (fixed for the block).
-  // KO operands: the column offset is the same for all chunks of a thread
-  // (NTHR is a multiple of R/8); chunk i covers k-row tid/(R/8) + i*NTHR/(R/8).
-  uint32_t oa[K_::a_ko ? 1 : CHA], ob[K_::b_ko ? 1 : CHB];
-  if constexpr (!K_::a_ko) {
+  // ---------------- DMA addressing ----------------
+  // DMA instruction i of wave w fills LDS row-block ci = i*NW + w (1 KiB) of
+  // an operand tile; lane l writes its 16 bytes at byte 1024*ci + 16*l.
+  //   KC tile [row][64]: row = 8*ci + l/8, physical chunk l%8 holds logical
+  //     chunk (l%8) ^ swz(row), i.e. global columns 8*logical .. +7 of the K tile.
+  //   KO tile [64 k][R]: k = (1024*ci + 16*l) / (2R); the 32-byte granule at
+  //     physical position g holds logical granule g ^ f(k).
+  const int w_uni = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t oa[DA], ob[DB];   // KC: byte offset of row + logical chunk; KO: byte offset of the columns
+  int ka[K_::a_ko ? DA : 1], kb[K_::b_ko ? DB : 1];   // KO: k-row of the chunk inside the tile
 #pragma unroll
-    for (int i = 0; i < CHA; ++i) {
-      const int q = tid + NTHR * i;
-      const int row = min(m0 + (q >> 3), mlim - 1);   // rows past the segment: any valid row
+  for (int i = 0; i < DA; ++i) {
+    const int ci = i * NW + w_uni;
+    if constexpr (!K_::a_ko) {
+      const int rl = 8 * ci + (lane >> 3);
+      const int row = min(m0 + rl, mlim - 1);   // rows past the segment: any valid row
+      const int chunk = (lane & 7) ^ ((rl ^ (rl >> 3)) & 7);
       uint32_t o;
       if constexpr (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) o = (uint32_t)(a.s2f[row] / k) * H;
       else if constexpr (KIND == KIND_FWD2) o = (uint32_t)row * I;
       else o = (uint32_t)row * 2 * I;
-      oa[i] = (o + (q & 7) * 8) * 2;
+      oa[i] = (o + chunk * 8) * 2;
+    } else {
+      const int p = 1024 * ci + 16 * lane;
+      const int kk = p / (BM * 2), byte = p % (BM * 2);
+      const int col = ((((byte >> 5) ^ ko_f<BM>(kk))) << 4) + ((byte >> 4) & 1) * 8;
+      ka[i] = kk;
+      oa[i] = min(m0 + col, mlim - 8) * 2;
     }
-  } else {
-    oa[0] = min(m0 + 8 * (tid % (BM / 8)), mlim - 8) * 2;
   }
-  if constexpr (!K_::b_ko) {
 #pragma unroll
-    for (int i = 0; i < CHB; ++i) {
-      const int q = tid + NTHR * i;
-      const int nn = q >> 3;
+  for (int i = 0; i < DB; ++i) {
+    const int ci = i * NW + w_uni;
+    if constexpr (!K_::b_ko) {
+      const int nl = 8 * ci + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((nl ^ (nl >> 3)) & 7);
       uint32_t o;
       if constexpr (KIND == KIND_FWD1) {
-        const int c = min(n0 + (nn & (BN / 2 - 1)), I - 1);
-        o = (uint32_t)((nn < BN / 2) ? c : I + c) * H;
+        const int c = min(n0 + (nl & (BN / 2 - 1)), I - 1);
+        o = (uint32_t)((nl < BN / 2) ? c : I + c) * H;
       } else {
-        o = (uint32_t)min(n0 + nn, H - 1) * I;
+        o = (uint32_t)min(n0 + nl, H - 1) * I;
       }
-      ob[i] = (o + (q & 7) * 8) * 2;
+      ob[i] = (o + chunk * 8) * 2;
+    } else {
+      const int p = 1024 * ci + 16 * lane;
+      const int kk = p / (BN * 2), byte = p % (BN * 2);
+      const int col = ((((byte >> 5) ^ ko_f<BN>(kk))) << 4) + ((byte >> 4) & 1) * 8;
+      kb[i] = kk;
+      ob[i] = min(n0 + col, nlim - 8) * 2;
     }
-  } else {
-    ob[0] = min(n0 + 8 * (tid % (BN / 8)), nlim - 8) * 2;
   }
-  static_assert(NTHR % (BM / 8) == 0 && NTHR % (BN / 8) == 0, "KO chunk columns must be per-thread constants");
-  const int krow_a0 = tid / (BM / 8), krow_b0 = tid / (BN / 8);
-  auto krow_a = [&](int i) { return krow_a0 + i * (NTHR / (BM / 8)); };
-  auto krow_b = [&](int i) { return krow_b0 + i * (NTHR / (BN / 8)); };
-
-  // byte offset of operand chunk i for K tile kt (kt may run past nk: the
-  // wgrad rows then read as zeros, the dense-K kinds re-read the last tile)
-  auto a_off = [&](int i, int kt) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (!K_::a_ko) {
-      return oa[i] + (uint32_t)min(kt, nk - 1) * (BK * 2);
-    } else {
-      const int rr = kt * BK + krow_a(i);
-      if constexpr (KIND == KIND_WGRAD2) {   // dY rows of the gathered tokens
-        const uint32_t t = s_tok[rr & (TOKTAB - 1)];
-        return (klo + rr < khi) ? t * 2 + oa[0] : OOB;
-      } else {                               // dG13 rows
-        return (klo + rr < khi) ? (uint32_t)(klo + rr) * (2 * I * 2) + oa[0] : OOB;
-      }
-    }
-  };
-  auto b_off = [&](int i, int kt) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (!K_::b_ko) {
-      return ob[i] + (uint32_t)min(kt, nk - 1) * (BK * 2);
-    } else if constexpr (K_::ragged_rows) {   // weights, dense K rows
-      const int kr = min(kt, nk - 1) * BK + krow_b(i);
-      return (uint32_t)kr * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + ob[0];
-    } else {
-      const int rr = kt * BK + krow_b(i);
-      if constexpr (KIND == KIND_WGRAD2) {   // Ag rows
-        return (klo + rr < khi) ? (uint32_t)(klo + rr) * (I * 2) + ob[0] : OOB;
-      } else {                               // x rows of the gathered tokens
-        const uint32_t t = s_tok[rr & (TOKTAB - 1)];
-        return (klo + rr < khi) ? t * 2 + ob[0] : OOB;
-      }
-    }
-  };
 
   // token offsets of gathered rows [klo + base, klo + base + TOKTAB)
   auto fill_tok = [&](int base) {
@@ -294,26 +287,44 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     }
   };
 
-  u32x4_t ra0[CHA], rb0[CHB], ra1[CHA], rb1[CHB];
-
-  auto load_tile = [&](u32x4_t (&ra)[CHA], u32x4_t (&rb)[CHB], int kt) __attribute__((always_inline)) {
+  const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)smem;
+  // issue the DMA of K tile kt into stage st (tiles past the end read zeros)
+  auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
+    const bool live = kt < nk;
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
 #pragma unroll
-    for (int i = 0; i < CHA; ++i) ra[i] = bload(ra_src, a_off(i, kt));
-#pragma unroll
-    for (int i = 0; i < CHB; ++i) rb[i] = bload(rb_src, b_off(i, kt));
-  };
-  auto store_tile = [&](const u32x4_t (&ra)[CHA], const u32x4_t (&rb)[CHB], int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CHA; ++i) {
-      const int q = tid + NTHR * i;
-      const int off = K_::a_ko ? ko_off<BM>(krow_a(i), 8 * (tid % (BM / 8))) : kc_off(q >> 3, q & 7);
-      *reinterpret_cast<u32x4_t*>(&sA[buf][off]) = ra[i];
+    for (int i = 0; i < DA; ++i) {
+      uint32_t off;
+      if constexpr (!K_::a_ko) {
+        off = live ? oa[i] + (uint32_t)kt * (BK * 2) : OOB;
+      } else {
+        const int rr = kt * BK + ka[i];
+        if constexpr (KIND == KIND_WGRAD2) {   // dY rows of the gathered tokens
+          const uint32_t t = s_tok[rr & (TOKTAB - 1)];
+          off = (klo + rr < khi) ? t * 2 + oa[i] : OOB;
+        } else {                               // dG13 rows
+          off = (klo + rr < khi) ? (uint32_t)(klo + rr) * (2 * I * 2) + oa[i] : OOB;
+        }
+      }
+      dma16(ra_src, off, __builtin_amdgcn_readfirstlane(sbase + (i * NW + w_uni) * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < CHB; ++i) {
-      const int q = tid + NTHR * i;
-      const int off = K_::b_ko ? ko_off<BN>(krow_b(i), 8 * (tid % (BN / 8))) : kc_off(q >> 3, q & 7);
-      *reinterpret_cast<u32x4_t*>(&sB[buf][off]) = rb[i];
+    for (int i = 0; i < DB; ++i) {
+      uint32_t off;
+      if constexpr (!K_::b_ko) {
+        off = live ? ob[i] + (uint32_t)kt * (BK * 2) : OOB;
+      } else if constexpr (K_::ragged_rows) {  // weights, dense K rows
+        off = live ? (uint32_t)(kt * BK + kb[i]) * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + ob[i] : OOB;
+      } else {
+        const int rr = kt * BK + kb[i];
+        if constexpr (KIND == KIND_WGRAD2) {   // Ag rows
+          off = (klo + rr < khi) ? (uint32_t)(klo + rr) * (I * 2) + ob[i] : OOB;
+        } else {                               // x rows of the gathered tokens
+          const uint32_t t = s_tok[rr & (TOKTAB - 1)];
+          off = (klo + rr < khi) ? t * 2 + ob[i] : OOB;
+        }
+      }
+      dma16(rb_src, off, __builtin_amdgcn_readfirstlane(sbase + BM * BK * 2 + (i * NW + w_uni) * 1024));
     }
   };
 
@@ -332,9 +343,9 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const bf16_t* As = sA[buf];
-    const bf16_t* Bs = sB[buf];
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const bf16_t* As = smem + st * STAGE;
+    const bf16_t* Bs = As + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       bf16x8_t af[FM], bfr[FN];
@@ -357,32 +368,33 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   };
 
   // ---------------- main loop ----------------
-  // tile kt is in LDS buffer kt&1 while tiles kt+1 and kt+2 are in registers
-  if (nk > 0) {
-    if constexpr (gathered_k) { fill_tok(0); __syncthreads(); }
-    load_tile(ra0, rb0, 0);
-    load_tile(ra1, rb1, 1);
-    store_tile(ra0, rb0, 0);
-    __syncthreads();
+  // S-1 tiles in flight; each iteration waits for its own tile's DMA, then a
+  // barrier publishes it and frees the stage computed last iteration, which
+  // receives tile kt + S - 1.
+  if constexpr (gathered_k) {
+    if (nk > 0) { fill_tok(0); __syncthreads(); }
   }
-  for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue_tile(st, st);
+  int st_c = 0, st_l = S - 1;   // stage to compute, stage to load
+  for (int kt = 0; kt < nk; ++kt) {
+    vm_wait<(S - 2) * (DA + DB)>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if constexpr (gathered_k) {
-      // the next loads reach row kt+2's table chunk: refill after everyone is done with the old one
-      if (((kt + 2) * BK) % TOKTAB == 0 && kt + 2 < nk) {
-        fill_tok((kt + 2) * BK);
+      const int kl = kt + S - 1;
+      if ((kl * BK) % TOKTAB == 0 && kl < nk) {   // rows of tile kl start a new table chunk
+        fill_tok(kl * BK);
         __syncthreads();
       }
     }
-    load_tile(ra0, rb0, kt + 2);
-    compute(0);
-    store_tile(ra1, rb1, 1);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    load_tile(ra1, rb1, kt + 3);
-    compute(1);
-    store_tile(ra0, rb0, 0);
-    __syncthreads();
+    issue_tile(kt + S - 1, st_l);
+    compute(st_c);
+    st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+    st_l = (st_l + 1 == S) ? 0 : st_l + 1;
   }
+  vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
+  __syncthreads();
 
   // ---------------- epilogues ----------------
   const int mrow = lane & 15;         // row inside a 16x16 block
@@ -486,7 +498,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     }
   } else {   // wgrad: fp32 output of one expert, staged through LDS so each
              // store instruction writes whole rows (full cache lines)
-    static_assert(BM * BN * 4 <= 2 * (BM + BN) * BK * 2, "fp32 tile must fit in the operand LDS");
+    static_assert(BM * BN * 4 <= S * STAGE * 2, "fp32 tile must fit in the operand LDS");
     float* s_out = reinterpret_cast<float*>(smem);
     constexpr int NQ = BN / 4;                             // 16-byte chunks per row
     auto out_off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ)) << 2); };
@@ -510,12 +522,12 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   }
 }
 
-// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD).
+// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).
 #ifndef MOE_CFG_ROW
-#define MOE_CFG_ROW 128, 128, 2, 2, 2
+#define MOE_CFG_ROW 128, 128, 2, 2, 2, 2
 #endif
 #ifndef MOE_CFG_WGRAD
-#define MOE_CFG_WGRAD 128, 128, 2, 2, 1
+#define MOE_CFG_WGRAD 128, 128, 2, 2, 2, 2
 #endif
 using CfgRow = TileCfg<MOE_CFG_ROW>;
 using CfgW = TileCfg<MOE_CFG_WGRAD>;
