@@ -24,7 +24,7 @@ CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
-    "-I" + os.path.join(ROOT, "include"),
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 
 

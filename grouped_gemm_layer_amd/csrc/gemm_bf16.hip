@@ -47,14 +47,13 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
-constexpr int BK = 64;
 constexpr int NXCD = 8;
 constexpr int TOKTAB = 2048;                 // gathered K rows per LDS token table
 constexpr uint32_t OOB = 0x80000000u;        // buffer offset that reads as zeros
 
-template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_>
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
   static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
   static constexpr int STAGES = ST_;    // LDS stages in flight (>= 2)
   static constexpr int NW = WGM * WGN, NTHR = 64 * NW;
@@ -67,6 +66,7 @@ struct TileCfg {
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(DA * NW * 1024 == BM * BK * 2 && DB * NW * 1024 == BN * BK * 2, "tiles must split into 1 KiB DMA rows");
   static_assert(STAGES >= 2, "need at least two LDS stages");
+  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -91,11 +91,20 @@ template <int N>
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 // ---- LDS layouts (element offsets) ----
-// KC: [row][64], 16-byte chunk c of row r stored at chunk c ^ ((r ^ r>>3) & 7)
-__device__ __forceinline__ int kc_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+// KC: [row][BK], 16-byte chunk c of row r stored at chunk c ^ swz(r).  With
+// 128-byte rows, swz = r & 7 makes the fragment reads (16 rows x one chunk per
+// 16 lanes) conflict-free on gfx950 (measured: ~190 B/clk/CU against ~113 for
+// swz = (r ^ r>>3) & 7, which conflicts two-way).
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row) {
+  if constexpr (BK == 64) return row & 7;
+  else return ((row >> 1) ^ (row >> 2)) & 3;
 }
-// KO: [64 k][R], 32-byte granule g of k-row k stored at granule g ^ f(k);
+template <int BK>
+__device__ __forceinline__ int kc_off(int row, int chunk) {
+  return row * BK + ((chunk ^ kc_swz<BK>(row)) << 3);
+}
+// KO: [BK k][R], 32-byte granule g of k-row k stored at granule g ^ f(k);
 // f spreads the 16 k-rows one transpose read touches over distinct granules.
 template <int R>
 __device__ __forceinline__ int ko_f(int k) {
@@ -109,8 +118,9 @@ __device__ __forceinline__ int ko_off(int k, int col) {
 }
 
 // MFMA operand fragment: 16 rows starting at `row0`, k = 32*ks + 8*(lane/16) + 0..7
+template <int BK>
 __device__ __forceinline__ bf16x8_t frag_kc(const bf16_t* lds, int row0, int ks, int lane) {
-  return *reinterpret_cast<const bf16x8_t*>(lds + kc_off(row0 + (lane & 15), ks * 4 + (lane >> 4)));
+  return *reinterpret_cast<const bf16x8_t*>(lds + kc_off<BK>(row0 + (lane & 15), ks * 4 + (lane >> 4)));
 }
 template <int R>
 __device__ __forceinline__ bf16x8_t frag_ko(const bf16_t* lds, int row0, int ks, int lane) {
@@ -153,7 +163,7 @@ template <int KIND, class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   using K_ = Kind<KIND>;
-  constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int DA = C::DA, DB = C::DB, NW = C::NW;
   constexpr bool gathered_k = K_::a_gk || K_::b_gk;
 
@@ -229,8 +239,9 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   // ---------------- DMA addressing ----------------
   // DMA instruction i of wave w fills LDS row-block ci = i*NW + w (1 KiB) of
   // an operand tile; lane l writes its 16 bytes at byte 1024*ci + 16*l.
-  //   KC tile [row][64]: row = 8*ci + l/8, physical chunk l%8 holds logical
-  //     chunk (l%8) ^ swz(row), i.e. global columns 8*logical .. +7 of the K tile.
+  //   KC tile [row][BK]: row = (1024/(2 BK))*ci + l/(BK/8), physical chunk
+  //     l%(BK/8) holds logical chunk (l%(BK/8)) ^ swz(row), i.e. global
+  //     columns 8*logical .. +7 of the K tile.
   //   KO tile [64 k][R]: k = (1024*ci + 16*l) / (2R); the 32-byte granule at
   //     physical position g holds logical granule g ^ f(k).
   const int w_uni = __builtin_amdgcn_readfirstlane(wave);
@@ -240,9 +251,9 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   for (int i = 0; i < DA; ++i) {
     const int ci = i * NW + w_uni;
     if constexpr (!K_::a_ko) {
-      const int rl = 8 * ci + (lane >> 3);
+      const int rl = (512 / BK) * ci + lane / (BK / 8);
       const int row = min(m0 + rl, mlim - 1);   // rows past the segment: any valid row
-      const int chunk = (lane & 7) ^ ((rl ^ (rl >> 3)) & 7);
+      const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(rl);
       uint32_t o;
       if constexpr (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) o = (uint32_t)(a.s2f[row] / k) * H;
       else if constexpr (KIND == KIND_FWD2) o = (uint32_t)row * I;
@@ -260,8 +271,8 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   for (int i = 0; i < DB; ++i) {
     const int ci = i * NW + w_uni;
     if constexpr (!K_::b_ko) {
-      const int nl = 8 * ci + (lane >> 3);
-      const int chunk = (lane & 7) ^ ((nl ^ (nl >> 3)) & 7);
+      const int nl = (512 / BK) * ci + lane / (BK / 8);
+      const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(nl);
       uint32_t o;
       if constexpr (KIND == KIND_FWD1) {
         const int c = min(n0 + (nl & (BN / 2 - 1)), I - 1);
@@ -343,55 +354,65 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) __attribute__((always_inline)) {
+  // All MFMA operands of one K tile are read into registers first, so the
+  // tile's LDS stage can be refilled while the MFMAs run.
+  bf16x8_t af[BK / 32][FM], bfr[BK / 32][FN];
+  auto load_frags = [&](int st) __attribute__((always_inline)) {
     const bf16_t* As = smem + st * STAGE;
     const bf16_t* Bs = As + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (K_::a_ko) af[i] = frag_ko<BM>(As, wm * WM + 16 * i, ks, lane);
-        else af[i] = frag_kc(As, wm * WM + 16 * i, ks, lane);
+        if constexpr (K_::a_ko) af[ks][i] = frag_ko<BM>(As, wm * WM + 16 * i, ks, lane);
+        else af[ks][i] = frag_kc<BK>(As, wm * WM + 16 * i, ks, lane);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if constexpr (K_::b_ko) bfr[j] = frag_ko<BN>(Bs, brow(j), ks, lane);
-        else bfr[j] = frag_kc(Bs, brow(j), ks, lane);
+        if constexpr (K_::b_ko) bfr[ks][j] = frag_ko<BN>(Bs, brow(j), ks, lane);
+        else bfr[ks][j] = frag_kc<BK>(Bs, brow(j), ks, lane);
       }
+    }
+  };
+  auto mfmas = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
   };
 
   // ---------------- main loop ----------------
-  // S-1 tiles in flight; each iteration waits for its own tile's DMA, then a
-  // barrier publishes it and frees the stage computed last iteration, which
-  // receives tile kt + S - 1.
+  // S tiles in flight.  Iteration kt: wait for this wave's DMA of tile kt; a
+  // barrier publishes it; every wave reads its operands into registers; a
+  // second barrier frees the stage, which receives tile kt + S while the
+  // MFMAs run from registers.
   if constexpr (gathered_k) {
     if (nk > 0) { fill_tok(0); __syncthreads(); }
   }
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue_tile(st, st);
-  int st_c = 0, st_l = S - 1;   // stage to compute, stage to load
+  for (int st = 0; st < S; ++st) issue_tile(st, st);
+  int st_c = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    vm_wait<(S - 2) * (DA + DB)>();
+    vm_wait<(S - 1) * (DA + DB)>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_frags(st_c);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (gathered_k) {
-      const int kl = kt + S - 1;
+      const int kl = kt + S;
       if ((kl * BK) % TOKTAB == 0 && kl < nk) {   // rows of tile kl start a new table chunk
         fill_tok(kl * BK);
         __syncthreads();
       }
     }
-    issue_tile(kt + S - 1, st_l);
-    compute(st_c);
+    issue_tile(kt + S, st_c);
+    mfmas();
     st_c = (st_c + 1 == S) ? 0 : st_c + 1;
-    st_l = (st_l + 1 == S) ? 0 : st_l + 1;
   }
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
@@ -524,10 +545,10 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).
 #ifndef MOE_CFG_ROW
-#define MOE_CFG_ROW 128, 128, 2, 2, 2, 2
+#define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
 #endif
 #ifndef MOE_CFG_WGRAD
-#define MOE_CFG_WGRAD 128, 128, 2, 2, 2, 2
+#define MOE_CFG_WGRAD 128, 128, 2, 2, 2, 4, 32
 #endif
 using CfgRow = TileCfg<MOE_CFG_ROW>;
 using CfgW = TileCfg<MOE_CFG_WGRAD>;
