@@ -1,0 +1,173 @@
+// Shared pieces of the grouped-GEMM kernels (bf16 and MXFP8): tile
+// configuration and the fused epilogues of the six GEMM kinds.  Internal.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace gg {
+
+constexpr int NXCD = 8;   // XCDs per MI355X; blocks are dealt to them round-robin
+
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
+  static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
+  static constexpr int STAGES = ST_;    // LDS stages in flight (>= 2)
+  static constexpr int NW = WGM * WGN, NTHR = 64 * NW;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  // 1 KiB LDS DMA instructions per wave per K tile, A and B operands
+  // (bf16 operands: BK elements = 2*BK bytes per row)
+  static constexpr int DA = BM * BK * 2 / 1024 / NW, DB = BN * BK * 2 / 1024 / NW;
+  // blocks resident on one XCD at a time: the size of the tile groups that share operands
+  static constexpr int GROUP = 32 * (4 * WPE) / NW;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(DA * NW * 1024 == BM * BK * 2 && DB * NW * 1024 == BN * BK * 2, "tiles must split into 1 KiB DMA rows");
+  static constexpr int SMEM_BYTES = STAGES * (BM + BN) * BK * 2;   // operand LDS of the kernel
+  static_assert(STAGES >= 2, "need at least two LDS stages");
+  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
+};
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+// Epilogue of one output tile.  acc[i][j][v] holds C[m][n] for
+//   m = m0 + wm*WM + 16 i + lane%16,  n = n0 + wn*WN + 16 j + 4*(lane/16) + v
+// (for the SwiGLU kind the first FN/2 column blocks are G1 and the rest the
+// matching G3 columns).  `smem` is the kernel's operand LDS, free by now.
+template <int KIND, class C>
+__device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)[C::FM][C::FN], void* smem,
+                                              int tid, int lane, int wm, int wn, int e, int m0, int mlim,
+                                              int n0, int nlim) {
+  constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  const int H = a.H, I = a.I;
+  // ---------------- epilogues ----------------
+  const int mrow = lane & 15;         // row inside a 16x16 block
+  const int ncol = 4 * (lane >> 4);   // first of 4 consecutive columns
+
+  if constexpr (KIND == KIND_FWD1) {
+    bf16_t* G13 = static_cast<bf16_t*>(a.G13);
+    bf16_t* Aout = static_cast<bf16_t*>(a.A);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WM + 16 * i + mrow;
+      if (m >= mlim) continue;
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const int c = n0 + wn * (WN / 2) + 16 * j + ncol;
+        if (c >= I) continue;
+        const f32x4_t g1 = acc[i][j], g3 = acc[i][j + FN / 2];
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = g1[v] * sigmoid_f32(g1[v]) * g3[v];
+        *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + c) = pack4(g1[0], g1[1], g1[2], g1[3]);
+        *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + I + c) = pack4(g3[0], g3[1], g3[2], g3[3]);
+        *reinterpret_cast<uint2*>(Aout + (size_t)m * I + c) = pack4(av[0], av[1], av[2], av[3]);
+      }
+    }
+  } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
+    bf16_t* out = static_cast<bf16_t*>(KIND == KIND_FWD2 ? a.O : a.dXp);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WM + 16 * i + mrow;
+      if (m >= mlim) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WN + 16 * j + ncol;
+        if (n >= nlim) continue;
+        const f32x4_t v = acc[i][j];
+        *reinterpret_cast<uint2*>(out + (size_t)m * H + n) = pack4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else if constexpr (KIND == KIND_DGRAD2) {
+    const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
+    bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
+    bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
+    // after the main loop's last barrier the A tiles are free: reused for the
+    // cross-wave reduction of the gate-gradient partials
+    float* s_part = reinterpret_cast<float*>(smem);
+    float psum[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      psum[i] = 0.f;
+      const int m = m0 + wm * WM + 16 * i + mrow;
+      if (m >= mlim) continue;
+      const float g = a.gate[a.s2f[m]];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WN + 16 * j + ncol;
+        if (n >= I) continue;
+        const uint2 r1 = *reinterpret_cast<const uint2*>(G13 + (size_t)m * 2 * I + n);
+        const uint2 r3 = *reinterpret_cast<const uint2*>(G13 + (size_t)m * 2 * I + I + n);
+        const float g1v[4] = {__uint_as_float(r1.x << 16), __uint_as_float(r1.x & 0xFFFF0000u),
+                              __uint_as_float(r1.y << 16), __uint_as_float(r1.y & 0xFFFF0000u)};
+        const float g3v[4] = {__uint_as_float(r3.x << 16), __uint_as_float(r3.x & 0xFFFF0000u),
+                              __uint_as_float(r3.y << 16), __uint_as_float(r3.y & 0xFFFF0000u)};
+        float d1[4], d3[4], ag[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float dap = acc[i][j][v];
+          const float s = sigmoid_f32(g1v[v]);
+          const float silu = g1v[v] * s;
+          const float av = silu * g3v[v];
+          psum[i] += dap * av;
+          const float da = g * dap;
+          d1[v] = da * g3v[v] * s * (1.f + g1v[v] * (1.f - s));
+          d3[v] = da * silu;
+          ag[v] = g * av;
+        }
+        *reinterpret_cast<uint2*>(dG13 + (size_t)m * 2 * I + n) = pack4(d1[0], d1[1], d1[2], d1[3]);
+        *reinterpret_cast<uint2*>(dG13 + (size_t)m * 2 * I + I + n) = pack4(d3[0], d3[1], d3[2], d3[3]);
+        *reinterpret_cast<uint2*>(Ag + (size_t)m * I + n) = pack4(ag[0], ag[1], ag[2], ag[3]);
+      }
+    }
+    // lanes sharing a row, then the WGN waves of a row block, in a fixed order
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      psum[i] += __shfl_xor(psum[i], 16);
+      psum[i] += __shfl_xor(psum[i], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) s_part[wn * BM + wm * WM + 16 * i + lane] = psum[i];
+    }
+    __syncthreads();
+    for (int ml = tid; ml < BM; ml += NTHR) {
+      const int m = m0 + ml;
+      if (m < mlim) {
+        float p = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::WGN; ++w) p += s_part[w * BM + ml];
+        a.dgate_part[(size_t)(n0 / BN) * a.M + m] = p;
+      }
+    }
+  } else {   // wgrad: fp32 output of one expert, staged through LDS so each
+             // store instruction writes whole rows (full cache lines)
+    static_assert(BM * BN * 4 <= C::SMEM_BYTES, "fp32 tile must fit in the operand LDS");
+    float* s_out = reinterpret_cast<float*>(smem);
+    constexpr int NQ = BN / 4;                             // 16-byte chunks per row
+    auto out_off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ)) << 2); };
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wm * WM + 16 * i + mrow;
+        const int q = (wn * WN + 16 * j + ncol) >> 2;
+        *reinterpret_cast<f32x4_t*>(&s_out[out_off(row, q)]) = acc[i][j];
+      }
+    __syncthreads();
+    float* out = (KIND == KIND_WGRAD2) ? a.dw2 + (size_t)e * H * I : a.dw13 + (size_t)e * 2 * I * H;
+    const int ld = (KIND == KIND_WGRAD2) ? I : H;
+    for (int c = tid; c < BM * NQ; c += NTHR) {
+      const int row = c / NQ, q = c % NQ;
+      const int m = m0 + row, n = n0 + 4 * q;
+      if (m < mlim && n < nlim)
+        *reinterpret_cast<f32x4_t*>(out + (size_t)m * ld + n) = *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]);
+    }
+  }
+}
+
+}  // namespace gg
+}  // namespace moe
