@@ -59,7 +59,7 @@ __all__ = [
     "Routing", "route", "silu", "sigmoid", "expert_forward", "expert_backward",
     "forward", "backward", "router_backward", "forward_with_gates",
     "e4m3fn_decode_table", "e4m3fn_encode", "mx_scale_exponent", "mx_quant_dequant",
-    "mx_quant_dequant_tokens", "backward_mxfp8",
+    "mx_quant_dequant_tokens", "expert_backward_mxfp8", "backward_mxfp8",
 ]
 
 
@@ -339,18 +339,44 @@ def mx_quant_dequant_tokens(a: np.ndarray, offsets: np.ndarray) -> np.ndarray:
     return out
 
 
-def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
-    """fp8_bwd backward with every backward GEMM operand replaced by
-    dequant(quant(.)) along that GEMM's K (R7).  The gate is applied after the
-    dgrad GEMM of W2 and folded into A for the W2 weight gradient.
+def expert_backward_mxfp8(dYp, Xp, g, w13e, w2e, fwd: dict) -> dict:
+    """One expert's share of the fp8_bwd backward (R7): the rows of one expert
+    segment, every backward GEMM operand replaced by dequant(quant(.)) along
+    that GEMM's K.  The gate is applied after the dgrad GEMM of W2 and folded
+    into A for the W2 weight gradient.
 
-    GEMMs (per expert e, rows R_e):
       dA'  = Q_H(dYp) Q_H(W2[e])            (K = H)
       dXp  = Q_2I(dG) Q_2I(W13[e])          (K = 2I)
       dW2  = Q_tok(dYp)^T Q_tok(g A)        (K = tokens of e)
       dW13 = Q_tok(dG)^T Q_tok(Xp)          (K = tokens of e)
-    dgate, dSwiGLU and the router gradient are computed from the unquantised
-    forward state."""
+
+    dgate and the SwiGLU derivative use the unquantised forward state `fwd`
+    (G1, G3, A of these rows).  Row-wise quantisation (along H or 2I) treats
+    every row on its own; the token blocks start at the segment's first row."""
+    dYp = np.asarray(dYp, dtype=np.float64)
+    Xp = np.asarray(Xp, dtype=np.float64)
+    n = dYp.shape[0]
+    seg = np.array([0, n])
+    qW2, _, _ = mx_quant_dequant(np.asarray(w2e, dtype=np.float64), axis=0)      # [H, I], K = H
+    qdYp, _, _ = mx_quant_dequant(dYp, axis=1)
+    dAp = qdYp @ qW2
+    A, G1, G3 = fwd["A"], fwd["G1"], fwd["G3"]
+    dgate = np.sum(dAp * A, axis=1)
+    dA = g[:, None] * dAp
+    s = sigmoid(G1)
+    dG = np.concatenate([dA * G3 * s * (1.0 + G1 * (1.0 - s)), dA * G1 * s], axis=1)
+    qW13, _, _ = mx_quant_dequant(np.asarray(w13e, dtype=np.float64), axis=0)   # [2I, H], K = 2I
+    qdG, _, _ = mx_quant_dequant(dG, axis=1)
+    dXp = qdG @ qW13
+    dW2 = mx_quant_dequant_tokens(dYp, seg).T @ mx_quant_dequant_tokens(g[:, None] * A, seg)
+    dW13 = mx_quant_dequant_tokens(dG, seg).T @ mx_quant_dequant_tokens(Xp, seg)
+    return {"dXp": dXp, "dgate": dgate, "dG": dG, "dW2": dW2, "dW13": dW13}
+
+
+def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
+    """fp8_bwd backward of the whole layer: expert_backward_mxfp8 on every
+    expert segment, then the unpermute-reduce of dX and the router backward
+    exactly as in backward()."""
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -358,38 +384,19 @@ def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
     M = T * k
     tok = r.sorted_to_flat // k
     g_sorted = r.gate.reshape(-1)[r.sorted_to_flat]
-    dYp = dy[tok]
-    Xp = x[tok]
     dXp = np.zeros((M, H))
     dW13 = np.zeros(w13.shape)
     dW2 = np.zeros(w2.shape)
     dgate_sorted = np.zeros(M)
-    qdYp_tok = mx_quant_dequant_tokens(dYp, r.offsets)
-    qXp_tok = mx_quant_dequant_tokens(Xp, r.offsets)
-    qdYp_h, _, _ = mx_quant_dequant(dYp, axis=1)
-    gA = g_sorted[:, None] * state["A"]
-    qgA_tok = mx_quant_dequant_tokens(gA, r.offsets)
-    dG = np.zeros((M, w13.shape[1]))
     for e, a, b in _segments(r):
         if b == a:
             continue
-        qW2, _, _ = mx_quant_dequant(np.asarray(w2[e], dtype=np.float64), axis=0)   # K = H
-        dAp = qdYp_h[a:b] @ qW2
-        A = state["A"][a:b]
-        G1, G3 = state["G1"][a:b], state["G3"][a:b]
-        dgate_sorted[a:b] = np.sum(dAp * A, axis=1)
-        dA = g_sorted[a:b, None] * dAp
-        s = sigmoid(G1)
-        dG[a:b] = np.concatenate([dA * G3 * s * (1.0 + G1 * (1.0 - s)), dA * G1 * s], axis=1)
-        dW2[e] = qdYp_tok[a:b].T @ qgA_tok[a:b]
-    qdG_tok = mx_quant_dequant_tokens(dG, r.offsets)
-    qdG_k, _, _ = mx_quant_dequant(dG, axis=1)
-    for e, a, b in _segments(r):
-        if b == a:
-            continue
-        qW13, _, _ = mx_quant_dequant(np.asarray(w13[e], dtype=np.float64), axis=0)  # K = 2I
-        dXp[a:b] = qdG_k[a:b] @ qW13
-        dW13[e] = qdG_tok[a:b].T @ qXp_tok[a:b]
+        fwd = {key: state[key][a:b] for key in ("A", "G1", "G3")}
+        out = expert_backward_mxfp8(dy[tok[a:b]], x[tok[a:b]], g_sorted[a:b], w13[e], w2[e], fwd)
+        dXp[a:b] = out["dXp"]
+        dgate_sorted[a:b] = out["dgate"]
+        dW2[e] = out["dW2"]
+        dW13[e] = out["dW13"]
     dX = dXp[r.flat_to_sorted].reshape(T, k, H).sum(axis=1)
     dgate = dgate_sorted[r.flat_to_sorted].reshape(T, k)
     dlogits = router_backward(r.gate, dgate, r.idx, E)

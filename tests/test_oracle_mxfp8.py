@@ -119,3 +119,40 @@ def test_quantised_backward_structure_with_identity_quantiser(monkeypatch):
     for key in ("dx", "dw13", "dw2", "dgate", "dlogits"):
         rel = np.max(np.abs(q[key] - g[key])) / np.max(np.abs(g[key]))
         assert rel < 1e-12, (key, rel)
+
+
+def test_quantised_operands_are_blocked_along_each_gemms_k(monkeypatch):
+    """Records every quantiser call of one expert's fp8_bwd backward: each GEMM
+    operand must be blocked along that GEMM's reduction dimension (H for the
+    dgrad of W2, 2I for the dgrad of W13, the expert's tokens for the weight
+    gradients), and the token-wise operands are dY, gate*A, dG13 and x."""
+    rng = np.random.default_rng(7)
+    n, H, I = 40, 64, 32
+    dYp, Xp = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    g = rng.uniform(0.1, 1.0, n)
+    w13e, w2e = rng.standard_normal((2 * I, H)), rng.standard_normal((H, I))
+    fwd = orc.expert_forward(Xp, w13e, w2e)
+    calls = []
+
+    def rec(a, axis=-1):
+        a = np.asarray(a, np.float64)
+        calls.append(("rows", a.shape, axis % a.ndim))
+        return a, None, None
+
+    def rec_tok(a, offsets):
+        a = np.asarray(a, np.float64)
+        calls.append(("tokens", a.shape, tuple(int(o) for o in offsets), a.copy()))
+        return a
+
+    monkeypatch.setattr(orc, "mx_quant_dequant", rec)
+    monkeypatch.setattr(orc, "mx_quant_dequant_tokens", rec_tok)
+    out = orc.expert_backward_mxfp8(dYp, Xp, g, w13e, w2e, fwd)
+    row_calls = sorted((c[1], c[2]) for c in calls if c[0] == "rows")
+    # W2 [H, I] along H (axis 0); dY [n, H] along H (axis 1); W13 [2I, H] along 2I (axis 0); dG [n, 2I] along 2I
+    assert row_calls == sorted([((H, I), 0), ((n, H), 1), ((2 * I, H), 0), ((n, 2 * I), 1)])
+    tok = [c for c in calls if c[0] == "tokens"]
+    assert len(tok) == 4 and all(c[2] == (0, n) for c in tok)
+    arrays = [c[3] for c in tok]
+    expected = [dYp, g[:, None] * fwd["A"], out["dG"], Xp]
+    for ref in expected:
+        assert any(a.shape == ref.shape and np.array_equal(a, ref) for a in arrays)
