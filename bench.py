@@ -25,10 +25,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd ms & TFLOPS, Qwen3-30B-A3B shape T=16384; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 operands)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
 BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
+BWD_KERNELS_FP8 = ["tile_table_b", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t", "quant_dg",
+                   "dgrad1", "unpermute_reduce", "router_bwd", "pad_offsets", "quant_dyt", "quant_agt", "wgrad2",
+                   "quant_dgt", "quant_xt", "wgrad1"]
 
 
 class HipEvents:
@@ -61,9 +65,15 @@ def gemm_flops(d):
 
 
 def hbm_bytes(d):
-    """Algorithmic HBM bytes of the memory-bound kernels (bf16 rows)."""
+    """Algorithmic HBM bytes of the memory-bound kernels (bf16 inputs, fp8
+    codes + one scale byte per 32 codes)."""
     rows = d.M * d.H * 2 + d.T * d.H * 2
-    return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4}
+    q = lambda n: n * 2 + n + n // 32            # read bf16, write codes + scales
+    H, I, E, M, T = d.H, d.I, d.E, d.M, d.T
+    return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4,
+            "quant_w2t": q(E * H * I), "quant_w13t": q(E * 2 * I * H), "quant_dy": q(T * H),
+            "quant_dg": q(M * 2 * I), "quant_dyt": q(M * H), "quant_agt": q(M * I), "quant_dgt": q(M * 2 * I),
+            "quant_xt": q(M * H)}
 
 
 def cpu_baseline(d, inp, n_tokens):
@@ -121,7 +131,12 @@ def main():
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    nf, nb = g.num_kernels("forward"), g.num_kernels("backward")
+    nf, nb = g.num_kernels(layer.dims, "forward"), g.num_kernels(layer.dims, "backward")
+    fp8_bwd = d.run_mode == "fp8_bwd"
+    bwd_names = BWD_KERNELS_FP8 if fp8_bwd else BWD_KERNELS
+    assert nf == len(FWD_KERNELS) and nb == len(bwd_names)
+    peak = {n: (PEAK_FP8_TFLOPS if fp8_bwd and n in ("dgrad2_dswiglu", "dgrad1", "wgrad2", "wgrad1")
+                else PEAK_BF16_TFLOPS) for n in FWD_KERNELS + bwd_names}
     K, W = args.steps, args.warmup
     fev = [ev.create(nf + 1) for _ in range(K)]
     bev = [ev.create(nb + 1) for _ in range(K)]
@@ -150,14 +165,14 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    names = FWD_KERNELS + BWD_KERNELS
+    names = FWD_KERNELS + bwd_names
     per = {n: [] for n in names}
     fwd_ms, bwd_ms, route_ms = [], [], []
     for i in range(K):
         for j in range(nf):
             per[FWD_KERNELS[j]].append(ev.elapsed(fev[i][j], fev[i][j + 1]))
         for j in range(nb):
-            per[BWD_KERNELS[j]].append(ev.elapsed(bev[i][j], bev[i][j + 1]))
+            per[bwd_names[j]].append(ev.elapsed(bev[i][j], bev[i][j + 1]))
         fwd_ms.append(ev.elapsed(fev[i][0], fev[i][nf]))
         bwd_ms.append(ev.elapsed(bev[i][0], bev[i][nb]))
         route_ms.append(rstart[i].elapsed_time(rend[i]))
@@ -169,7 +184,7 @@ def main():
         ent = {"ms": round(avg[n], 4)}
         if n in flops:
             tf = flops[n] / (avg[n] * 1e-3) / 1e12
-            ent.update(tflops=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+            ent.update(tflops=round(tf, 1), mfma_frac=round(tf / peak[n], 4))
         if n in hbm:
             gbs = hbm[n] / (avg[n] * 1e-3) / 1e9
             ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
@@ -178,14 +193,14 @@ def main():
     value = total_flops / (ms_per_step * 1e-3) / 1e12
     dom = max(flops, key=lambda n: avg[n])
     dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2), "peak": peak[dom],
+                "unit": "TFLOP/s", "frac": round(dom_tf / peak[dom], 4), "traffic": None,
                 "flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
     gemm_ms = sum(avg[n] for n in flops)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if d.run_mode != "fp32" else "f32", "data": "synthetic",
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8_bwd": "bf16 fwd + mxfp8 bwd"}[d.run_mode], "data": "synthetic",
         "config": {"workload": mi.CONFIG_NAMES[args.config], "T": d.T, "H": d.H, "I": d.I, "E": d.E,
                    "k": d.k, "mode": d.run_mode, "seed": seed},
         "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4),
@@ -193,7 +208,7 @@ def main():
         "fwd_tflops": round(6.0 * d.M * d.H * d.I / (np.mean(fwd_ms) * 1e-3) / 1e12, 1),
         "bwd_tflops": round(12.0 * d.M * d.H * d.I / (np.mean(bwd_ms) * 1e-3) / 1e12, 1),
         "gemm_tflops": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
-        "gemm_mfma_frac": round(total_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm_mfma_frac": round(sum(flops[n] / (peak[n] * 1e12) for n in flops) / (gemm_ms * 1e-3), 4),
         "kernels": kernels, "roofline": roofline, "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -9,6 +9,8 @@ Names follow the C ABI in include/moe.h:
     route(dims, logits, routing, ws)
     forward(dims, x, w13, w2, routing, y, saved, ws)
     backward(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws)
+    mxfp8_quantize(src, along, codes, scales)
+    mxfp8_quantize_grouped(src, offsets, capacity, pad_off, codes, scales)
 plus allocation helpers (alloc_routing, alloc_workspace) and MoeLayer, a
 small holder that owns the buffers of one shape.
 """
@@ -20,7 +22,8 @@ import os
 __all__ = [
     "MODE_FP32", "MODE_BF16", "MODE_MXFP8", "MODE_FP8_BWD", "Dims", "RoutingBuffers",
     "MoeError", "lib_path", "load_library", "workspace_size", "route", "forward", "backward",
-    "alloc_routing", "alloc_workspace", "status_str", "MoeLayer", "num_kernels",
+    "alloc_routing", "alloc_workspace", "status_str", "MoeLayer", "num_kernels", "mxfp8_quantize",
+    "mxfp8_quantize_grouped", "mxfp8_grouped_capacity",
 ]
 
 MODE_FP32, MODE_BF16, MODE_MXFP8, MODE_FP8_BWD = 0, 1, 2, 3
@@ -86,8 +89,15 @@ def load_library():
     lib.moe_backward_timed.argtypes = lib.moe_backward.argtypes + [vp, ctypes.c_int]
     lib.moe_forward_timed.restype = ctypes.c_int
     lib.moe_backward_timed.restype = ctypes.c_int
-    lib.moe_num_kernels.argtypes = [ctypes.c_int]
+    lib.moe_num_kernels.argtypes = [ctypes.POINTER(Dims), ctypes.c_int]
     lib.moe_num_kernels.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_mxfp8_quantize.restype = ctypes.c_int
+    lib.moe_mxfp8_quantize_grouped.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, vp, vp]
+    lib.moe_mxfp8_quantize_grouped.restype = ctypes.c_int
+    lib.moe_mxfp8_grouped_capacity.argtypes = [i32, i32]
+    lib.moe_mxfp8_grouped_capacity.restype = sz
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -179,8 +189,33 @@ def backward(dims: Dims, dy, x, w13, w2, routing: RoutingBuffers, saved, dx, dw1
         _check(lib.moe_backward_timed(*args, events, len(events)), "moe_backward_timed")
 
 
-def num_kernels(which: str) -> int:
-    return load_library().moe_num_kernels({"route": 0, "forward": 1, "backward": 2}[which])
+def num_kernels(dims: Dims, which: str) -> int:
+    n = load_library().moe_num_kernels(ctypes.byref(dims), {"route": 0, "forward": 1, "backward": 2}[which])
+    if n < 0:
+        raise MoeError(2, "moe_num_kernels")
+    return n
+
+
+def mxfp8_quantize(src, along: int, codes, scales, stream=None):
+    """src: bf16 [rows, cols]; along=1 -> codes [rows, cols], scales [rows, cols/32];
+    along=0 -> codes [cols, rows], scales [cols, rows/32] (uint8 tensors)."""
+    rows, cols = src.shape
+    _check(load_library().moe_mxfp8_quantize(_ptr(src), rows, cols, along, _ptr(codes), _ptr(scales),
+                                             _stream(stream)), "moe_mxfp8_quantize")
+
+
+def mxfp8_grouped_capacity(rows: int, E: int) -> int:
+    return int(load_library().moe_mxfp8_grouped_capacity(rows, E))
+
+
+def mxfp8_quantize_grouped(src, offsets, capacity: int, pad_off, codes, scales, stream=None):
+    """src: bf16 [rows, cols] in expert order (offsets int32 [E+1]); codes
+    [cols, capacity], scales [cols, capacity/32] (uint8), pad_off int32 [E+1]."""
+    rows, cols = src.shape
+    E = offsets.numel() - 1
+    _check(load_library().moe_mxfp8_quantize_grouped(_ptr(src), rows, cols, _ptr(offsets), E, capacity,
+                                                     _ptr(pad_off), _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_mxfp8_quantize_grouped")
 
 
 class MoeLayer:

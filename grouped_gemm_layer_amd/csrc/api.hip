@@ -16,12 +16,18 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 inline bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
+inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
 struct Sizes {
   size_t route_ws, saved, fwd_ws, bwd_ws;
   // carving offsets
   size_t r_partials, r_bases;
   size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
   size_t b_tile_e, b_tile_r, b_tile_x, b_dG13, b_Ag, b_dXp, b_part;
+  // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
+  size_t Mp;
+  size_t q_pad, q_dy, s_dy, q_w2t, s_w2t, q_dg, s_dg, q_w13t, s_w13t;
+  size_t q_dyt, s_dyt, q_agt, s_agt, q_dgt, s_dgt, q_xt, s_xt;
 };
 
 moe_status check_dims(const moe_dims* d) {
@@ -29,9 +35,19 @@ moe_status check_dims(const moe_dims* d) {
   if (d->T <= 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k <= 0 || d->k > d->E) return MOE_ERR_DIMS;
   if ((int64_t)d->T * d->k > INT32_MAX) return MOE_ERR_DIMS;
   if ((int64_t)d->E * 2 * d->I * d->H > ((int64_t)1 << 40)) return MOE_ERR_DIMS;
-  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_FP8_BWD)
+    return MOE_ERR_UNSUPPORTED;
   if (d->H % 64 != 0 || d->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->mode == MOE_MODE_FP8_BWD && d->H % MX_KTILE != 0) return MOE_ERR_UNSUPPORTED;
   if (d->E > 512 || d->k > 32) return MOE_ERR_UNSUPPORTED;
+  // every per-operand buffer is addressed with 32-bit byte offsets
+  const int64_t M = (int64_t)d->T * d->k;
+  const int64_t wide = d->H > 2 * d->I ? d->H : 2 * d->I;
+  const int64_t es = d->mode == MOE_MODE_FP32 ? 4 : 2;
+  if (M * wide * es >= ((int64_t)1 << 31) || (int64_t)2 * d->I * d->H * es >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (d->mode == MOE_MODE_FP8_BWD && (int64_t)mx_token_capacity((size_t)M, d->E) * wide >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -39,15 +55,16 @@ Sizes compute_sizes(const moe_dims* d) {
   Sizes s{};
   const size_t M = (size_t)d->T * d->k;
   const size_t es = (d->mode == MOE_MODE_FP32) ? 4 : 2;
-  const bool bf16 = d->mode != MOE_MODE_FP32;
-  const int bm = row_tile_m(bf16);
-  const size_t max_tiles = (size_t)max_row_tiles((int)M, d->E, bm);
+  const size_t max_tiles = (size_t)max_row_tiles((int)M, d->E, fwd_row_tile_m(d->mode));
+  const size_t max_tiles_b = (size_t)max_row_tiles((int)M, d->E, bwd_row_tile_m(d->mode));
   const size_t nblk = (size_t)route_num_blocks((int)M);
   size_t o = 0;
   s.r_partials = o; o += align_up(nblk * d->E * 4);
   s.r_bases = o;    o += align_up(nblk * d->E * 4);
   s.route_ws = o;
-  s.saved = align_up(M * 2 * d->I * es);
+  // fp8_bwd keeps the quantisers' inputs (G13, dG13, gate*A) in fp32
+  const size_t es_q = (d->mode == MOE_MODE_FP8_BWD) ? 4 : es;
+  s.saved = align_up(M * 2 * d->I * es_q);
   o = 0;
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
@@ -56,13 +73,28 @@ Sizes compute_sizes(const moe_dims* d) {
   s.f_O = o;      o += align_up(M * d->H * es);
   s.fwd_ws = o;
   o = 0;
-  s.b_tile_e = o; o += align_up(max_tiles * 4);
-  s.b_tile_r = o; o += align_up(max_tiles * 4);
+  s.b_tile_e = o; o += align_up(max_tiles_b * 4);
+  s.b_tile_r = o; o += align_up(max_tiles_b * 4);
   s.b_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
-  s.b_dG13 = o;   o += align_up(M * 2 * d->I * es);
-  s.b_Ag = o;     o += align_up(M * d->I * es);
+  s.b_dG13 = o;   o += align_up(M * 2 * d->I * es_q);
+  s.b_Ag = o;     o += align_up(M * d->I * es_q);
   s.b_dXp = o;    o += align_up(M * d->H * es);
-  s.b_part = o;   o += align_up((size_t)dgrad2_parts(bf16, d->I) * M * 4);
+  s.b_part = o;   o += align_up((size_t)dgrad2_parts(d->mode, d->I) * M * 4);
+  if (d->mode == MOE_MODE_FP8_BWD) {
+    const size_t T = d->T, H = d->H, I = d->I, E = d->E;
+    const size_t Mp = mx_token_capacity(M, d->E);
+    s.Mp = Mp;
+    auto take = [&](size_t& at_, size_t bytes) { at_ = o; o += align_up(bytes); };
+    take(s.q_pad, (E + 1) * 4);
+    take(s.q_dy, T * H);          take(s.s_dy, T * H / 32);
+    take(s.q_w2t, E * I * H);     take(s.s_w2t, E * I * H / 32);
+    take(s.q_dg, M * 2 * I);      take(s.s_dg, M * 2 * I / 32);
+    take(s.q_w13t, E * H * 2 * I); take(s.s_w13t, E * H * 2 * I / 32);
+    take(s.q_dyt, H * Mp);        take(s.s_dyt, H * Mp / 32);
+    take(s.q_agt, I * Mp);        take(s.s_agt, I * Mp / 32);
+    take(s.q_dgt, 2 * I * Mp);    take(s.s_dgt, 2 * I * Mp / 32);
+    take(s.q_xt, H * Mp);         take(s.s_xt, H * Mp / 32);
+  }
   s.bwd_ws = o;
   return s;
 }
@@ -77,8 +109,6 @@ moe_status check_routing(const moe_routing* r) {
   return MOE_OK;
 }
 
-inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
-
 LayerArgs base_args(const moe_dims* d, const moe_routing* r) {
   LayerArgs a{};
   a.T = d->T; a.H = d->H; a.I = d->I; a.E = d->E; a.k = d->k; a.M = d->T * d->k;
@@ -92,6 +122,23 @@ LayerArgs base_args(const moe_dims* d, const moe_routing* r) {
 inline hipError_t gemm(bool bf16, GemmKind kind, const LayerArgs& a, hipStream_t s) {
   return bf16 ? launch_gemm_bf16(kind, a, s) : launch_gemm_fp32(kind, a, s);
 }
+
+Mx8Args mx8_args(const Sizes& s, void* ws) {
+  auto u8 = [&](size_t off) { return reinterpret_cast<const uint8_t*>(at(ws, off)); };
+  Mx8Args q{};
+  q.pad_off = reinterpret_cast<const int32_t*>(at(ws, s.q_pad));
+  q.Mp = (int)s.Mp;
+  q.qdy = u8(s.q_dy);     q.sdy = u8(s.s_dy);
+  q.qw2t = u8(s.q_w2t);   q.sw2t = u8(s.s_w2t);
+  q.qdg = u8(s.q_dg);     q.sdg = u8(s.s_dg);
+  q.qw13t = u8(s.q_w13t); q.sw13t = u8(s.s_w13t);
+  q.qdyt = u8(s.q_dyt);   q.sdyt = u8(s.s_dyt);
+  q.qagt = u8(s.q_agt);   q.sagt = u8(s.s_agt);
+  q.qdgt = u8(s.q_dgt);   q.sdgt = u8(s.s_dgt);
+  q.qxt = u8(s.q_xt);     q.sxt = u8(s.s_xt);
+  return q;
+}
+inline uint8_t* mut(const uint8_t* p) { return const_cast<uint8_t*>(p); }
 
 // Optional event marks for benchmarking: events[0] before the first kernel,
 // events[i + 1] after kernel i (stream-ordered; no synchronisation).
@@ -110,6 +157,11 @@ struct Marks {
 constexpr int kRouteKernels = 4;      // topk+gate, histogram, scan, scatter
 constexpr int kForwardKernels = 4;    // tile table, GEMM1+SwiGLU, GEMM2, combine
 constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13
+// fp8_bwd: tile table, quant W2^T, quant dY, dgrad W2, quant W13^T, quant dG13,
+// dgrad W13, unpermute, router, padded offsets, quant dY^T, quant (gA)^T,
+// wgrad W2, quant dG13^T, quant x^T, wgrad W13
+constexpr int kBackwardKernelsMx8 = 16;
+inline int backward_kernels(int mode) { return mode == MOE_MODE_FP8_BWD ? kBackwardKernelsMx8 : kBackwardKernels; }
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
@@ -169,13 +221,14 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   LayerArgs a = base_args(dims, routing);
   a.x = x; a.w13 = w13; a.w2 = w2;
   a.G13 = saved;
+  a.g13_f32 = dims->mode == MOE_MODE_FP8_BWD;
   a.A = at(ws, s.f_A);
   a.O = at(ws, s.f_O);
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.f_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.f_tile_r));
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.f_tile_x));
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
-  const int bm = row_tile_m(bf16);
+  const int bm = fwd_row_tile_m(dims->mode);
   hipError_t e = mk.mark();
   if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream);
   if (e == hipSuccess) e = mk.mark();
@@ -221,32 +274,66 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.b_tile_r));
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
-  const int bm = row_tile_m(bf16);
+  const int bm = bwd_row_tile_m(dims->mode);
+  const bool mx8 = dims->mode == MOE_MODE_FP8_BWD;
+  const Mx8Args q = mx8 ? mx8_args(s, ws) : Mx8Args{};
+  const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
+  const bf16_t* x16 = static_cast<const bf16_t*>(x);
   // activation-gradient chain first; the weight gradients do not feed it
   hipError_t e = mk.mark();
-  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_DGRAD2, a, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_DGRAD1, a, stream);
-  if (e == hipSuccess) e = mk.mark();
+  auto step = [&](hipError_t r) {   // record kernel completion, keep the first error
+    if (e == hipSuccess) e = r;
+    if (e == hipSuccess) e = mk.mark();
+  };
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream));
+  if (mx8) {
+    if (e == hipSuccess)
+      step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, mut(q.qw2t), mut(q.sw2t), stream));
+    if (e == hipSuccess) step(launch_mx_quant_rows(dy16, a.T, a.H, nullptr, 1, mut(q.qdy), mut(q.sdy), stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_DGRAD2, a, q, stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, mut(q.qw13t), mut(q.sw13t),
+                                  stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_rows(static_cast<const float*>(a.dG13), a.M, 2 * a.I, nullptr, 1, mut(q.qdg),
+                                mut(q.sdg), stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_DGRAD1, a, q, stream));
+  } else {
+    if (e == hipSuccess) step(gemm(bf16, KIND_DGRAD2, a, stream));
+    if (e == hipSuccess) step(gemm(bf16, KIND_DGRAD1, a, stream));
+  }
   if (e == hipSuccess) {
     if (bf16)
-      e = launch_combine<bf16_t>(static_cast<const bf16_t*>(a.dXp), a.f2s, nullptr, a.T, a.k, a.H,
-                                 static_cast<bf16_t*>(dx), stream);
+      step(launch_combine<bf16_t>(static_cast<const bf16_t*>(a.dXp), a.f2s, nullptr, a.T, a.k, a.H,
+                                  static_cast<bf16_t*>(dx), stream));
     else
-      e = launch_combine<float>(static_cast<const float*>(a.dXp), a.f2s, nullptr, a.T, a.k, a.H,
-                                static_cast<float*>(dx), stream);
+      step(launch_combine<float>(static_cast<const float*>(a.dXp), a.f2s, nullptr, a.T, a.k, a.H,
+                                 static_cast<float*>(dx), stream));
   }
-  if (e == hipSuccess) e = mk.mark();
   if (e == hipSuccess)
-    e = launch_router_bwd(a.dgate_part, dgrad2_parts(bf16, a.I), a.f2s, a.gate, routing->topk_idx, a.T, a.k,
-                          a.E, a.M, dgate, dlogits, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_WGRAD2, a, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_WGRAD1, a, stream);
-  if (e == hipSuccess) e = mk.mark();
+    step(launch_router_bwd(a.dgate_part, dgrad2_parts(dims->mode, a.I), a.f2s, a.gate, routing->topk_idx, a.T,
+                           a.k, a.E, a.M, dgate, dlogits, stream));
+  if (mx8) {
+    int32_t* pad = const_cast<int32_t*>(q.pad_off);
+    if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, pad, stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_tokens_t(dy16, a.H, a.s2f, a.k, a.offsets, pad, a.E, q.Mp, mut(q.qdyt), mut(q.sdyt),
+                                    stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_tokens_t(static_cast<const float*>(a.Ag), a.I, nullptr, 1, a.offsets, pad, a.E, q.Mp,
+                                    mut(q.qagt), mut(q.sagt), stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_WGRAD2, a, q, stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_tokens_t(static_cast<const float*>(a.dG13), 2 * a.I, nullptr, 1, a.offsets, pad, a.E,
+                                    q.Mp, mut(q.qdgt), mut(q.sdgt), stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_tokens_t(x16, a.H, a.s2f, a.k, a.offsets, pad, a.E, q.Mp, mut(q.qxt), mut(q.sxt),
+                                    stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_WGRAD1, a, q, stream));
+  } else {
+    if (e == hipSuccess) step(gemm(bf16, KIND_WGRAD2, a, stream));
+    if (e == hipSuccess) step(gemm(bf16, KIND_WGRAD1, a, stream));
+  }
   return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -267,8 +354,9 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
                        Marks{nullptr, 0, 0, stream});
 }
 
-int moe_num_kernels(int which) {
-  return which == 0 ? kRouteKernels : which == 1 ? kForwardKernels : which == 2 ? kBackwardKernels : -1;
+int moe_num_kernels(const moe_dims* dims, int which) {
+  if (check_dims(dims) != MOE_OK) return -1;
+  return which == 0 ? kRouteKernels : which == 1 ? kForwardKernels : which == 2 ? backward_kernels(dims->mode) : -1;
 }
 
 moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
@@ -285,9 +373,46 @@ moe_status moe_backward_timed(const moe_dims* dims, const void* dy, const void* 
                               float* dw13, float* dw2, float* dgate, float* dlogits, void* ws, size_t ws_bytes,
                               hipStream_t stream, hipEvent_t* events, int n_events) {
   if (!events) return MOE_ERR_NULL;
-  if (n_events < kBackwardKernels + 1) return MOE_ERR_DIMS;
+  if (check_dims(dims) == MOE_OK && n_events < backward_kernels(dims->mode) + 1) return MOE_ERR_DIMS;
   return backward_impl(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws, ws_bytes, stream,
                        Marks{events, n_events, 0, stream});
+}
+
+moe_status moe_mxfp8_quantize(const void* src, int32_t rows, int32_t cols, int32_t along, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  if (!src || !codes || !scales) return MOE_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || (along != 0 && along != 1)) return MOE_ERR_DIMS;
+  if (along == 1 && cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (along == 0 && rows % MX_KTILE != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)rows * cols * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(src) || !aligned(codes) || !aligned(scales)) return MOE_ERR_ALIGN;
+  const bf16_t* s16 = static_cast<const bf16_t*>(src);
+  const hipError_t e = along == 1 ? launch_mx_quant_rows(s16, rows, cols, nullptr, 1, codes, scales, stream)
+                                  : launch_mx_quant_cols_t(s16, 1, rows, cols, codes, scales, stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status moe_mxfp8_quantize_grouped(const void* src, int32_t rows, int32_t cols, const int32_t* offsets,
+                                      int32_t E, int32_t capacity, int32_t* pad_off, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t stream) {
+  if (!src || !offsets || !pad_off || !codes || !scales) return MOE_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || E <= 0) return MOE_ERR_DIMS;
+  if (E > 512 || capacity % MX_KTILE != 0 || (size_t)capacity < mx_token_capacity((size_t)rows, E))
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)rows * cols * 2 >= ((int64_t)1 << 31) || (int64_t)capacity * cols >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (!aligned(src) || !aligned(offsets) || !aligned(pad_off) || !aligned(codes) || !aligned(scales))
+    return MOE_ERR_ALIGN;
+  hipError_t e = launch_pad_offsets(offsets, E, pad_off, stream);
+  if (e == hipSuccess)
+    e = launch_mx_quant_tokens_t(static_cast<const bf16_t*>(src), cols, nullptr, 1, offsets, pad_off, E, capacity,
+                                 codes, scales, stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+size_t moe_mxfp8_grouped_capacity(int32_t rows, int32_t E) {
+  if (rows <= 0 || E <= 0) return 0;
+  return mx_token_capacity((size_t)rows, E);
 }
 
 const char* moe_status_str(moe_status status) {

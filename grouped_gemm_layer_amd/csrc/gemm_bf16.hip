@@ -45,34 +45,14 @@ namespace {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
 constexpr int TOKTAB = 2048;                 // gathered K rows per LDS token table
-constexpr uint32_t OOB = 0x80000000u;        // buffer offset that reads as zeros
-
 using gg::TileCfg;
 using gg::NXCD;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
-}
-
-// 16-byte buffer load straight into LDS: lane l writes LDS bytes [m0 + 16 l, +16).
-// Issued as inline assembly so that the compiler neither tracks nor waits on
-// it; completion is awaited explicitly (vm_wait) before the barrier that
-// publishes a stage.  An offset past the buffer's end stores zeros.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t lds_m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(byte_off), "s"(r), "s"(lds_m0) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-template <int N>
-__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+using gg::OOB;
+using gg::make_rsrc;
+using gg::dma16;
+using gg::vm_wait;
 
 // ---- LDS layouts (element offsets) ----
 // KC: [row][BK], 16-byte chunk c of row r stored at chunk c ^ swz(r).  With
@@ -162,22 +142,12 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   if (L >= tiles_total) return;
   int e, m0, mlim, n0, klo = 0, khi = 0, nk;
   if constexpr (K_::ragged_rows) {
-    // Logical order: expert-major; inside an expert, groups of gn column
-    // tiles, and inside a group all of the expert's row tiles with the gn
-    // columns fastest, so that about one XCD's worth of concurrent blocks
-    // shares the same token rows and weight rows.
-    e = a.tile_expert[L / n_tiles];
-    if (e < 0) return;
-    const int t0 = a.expert_tile0[e];
-    const int me = a.expert_tile0[e + 1] - t0;            // row tiles of this expert
-    const int local = L - t0 * n_tiles;
-    const int gn = max(1, min(n_tiles, C::GROUP / me));
-    const int ng = local / (me * gn);
-    const int gs = min(gn, n_tiles - ng * gn);
-    const int rem = local - ng * me * gn;
-    const int nt = ng * gn + rem % gs;
-    m0 = a.tile_row0[t0 + rem / gs];
-    mlim = a.offsets[e + 1];
+    gg::RowTile rt;
+    if (!gg::decode_row_tile(a, L, n_tiles, C::GROUP, rt)) return;
+    e = rt.e;
+    m0 = rt.m0;
+    mlim = rt.mlim;
+    const int nt = rt.nt;
     n0 = nt * (KIND == KIND_FWD1 ? BN / 2 : BN);
     const int Kd = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) ? H : (KIND == KIND_FWD2 ? I : 2 * I);
     nk = Kd / BK;

@@ -8,6 +8,56 @@ namespace moe {
 namespace gg {
 
 constexpr int NXCD = 8;   // XCDs per MI355X; blocks are dealt to them round-robin
+constexpr uint32_t OOB = 0x80000000u;   // buffer offset that reads as zeros
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer loads straight into LDS: lane l writes LDS bytes [m0 + W l, +W) for
+// W = 16 (dma16) or 4 (dma4).  Issued as inline assembly so that the compiler
+// neither tracks nor waits on them; completion is awaited explicitly
+// (vm_wait) before the barrier that publishes a stage.  An offset past the
+// buffer's end stores zeros.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t lds_m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(byte_off), "s"(r), "s"(lds_m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t lds_m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(byte_off), "s"(r), "s"(lds_m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// Logical tile L of a row-ragged GEMM -> (expert, first row, column tile).
+// Order: expert-major; inside an expert, groups of gn column tiles, and inside
+// a group all of the expert's row tiles with the gn columns fastest, so that
+// about one XCD's worth of concurrent blocks (`group` blocks) shares the same
+// token rows and weight rows.  Returns false for an unused tile.
+struct RowTile { int e, m0, mlim, nt; };
+__device__ __forceinline__ bool decode_row_tile(const LayerArgs& a, int L, int n_tiles, int group, RowTile& t) {
+  const int e = a.tile_expert[L / n_tiles];
+  if (e < 0) return false;
+  const int t0 = a.expert_tile0[e];
+  const int me = a.expert_tile0[e + 1] - t0;            // row tiles of this expert
+  const int local = L - t0 * n_tiles;
+  const int gn = max(1, min(n_tiles, group / me));
+  const int ng = local / (me * gn);
+  const int gs = min(gn, n_tiles - ng * gn);
+  const int rem = local - ng * me * gn;
+  t.e = e;
+  t.nt = ng * gn + rem % gs;
+  t.m0 = a.tile_row0[t0 + rem / gs];
+  t.mlim = a.offsets[e + 1];
+  return true;
+}
 
 template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64>
 struct TileCfg {
@@ -37,7 +87,7 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 //   m = m0 + wm*WM + 16 i + lane%16,  n = n0 + wn*WN + 16 j + 4*(lane/16) + v
 // (for the SwiGLU kind the first FN/2 column blocks are G1 and the rest the
 // matching G3 columns).  `smem` is the kernel's operand LDS, free by now.
-template <int KIND, class C>
+template <int KIND, class C, bool F32IO = false>
 __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)[C::FM][C::FN], void* smem,
                                               int tid, int lane, int wm, int wn, int e, int m0, int mlim,
                                               int n0, int nlim) {
@@ -48,7 +98,6 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
   const int ncol = 4 * (lane >> 4);   // first of 4 consecutive columns
 
   if constexpr (KIND == KIND_FWD1) {
-    bf16_t* G13 = static_cast<bf16_t*>(a.G13);
     bf16_t* Aout = static_cast<bf16_t*>(a.A);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -62,8 +111,15 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         float av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) av[v] = g1[v] * sigmoid_f32(g1[v]) * g3[v];
-        *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + c) = pack4(g1[0], g1[1], g1[2], g1[3]);
-        *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + I + c) = pack4(g3[0], g3[1], g3[2], g3[3]);
+        if (a.g13_f32) {   // saved state kept in fp32 (MXFP8 backward quantises from it)
+          float* G13 = static_cast<float*>(a.G13);
+          *reinterpret_cast<f32x4_t*>(G13 + (size_t)m * 2 * I + c) = g1;
+          *reinterpret_cast<f32x4_t*>(G13 + (size_t)m * 2 * I + I + c) = g3;
+        } else {
+          bf16_t* G13 = static_cast<bf16_t*>(a.G13);
+          *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + c) = pack4(g1[0], g1[1], g1[2], g1[3]);
+          *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + I + c) = pack4(g3[0], g3[1], g3[2], g3[3]);
+        }
         *reinterpret_cast<uint2*>(Aout + (size_t)m * I + c) = pack4(av[0], av[1], av[2], av[3]);
       }
     }
@@ -82,9 +138,8 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       }
     }
   } else if constexpr (KIND == KIND_DGRAD2) {
-    const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
-    bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
-    bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
+    // F32IO: G13 is read and dG13, gate*A are written in fp32 (inputs of the
+    // MXFP8 quantisers), else all three are bf16
     // after the main loop's last barrier the A tiles are free: reused for the
     // cross-wave reduction of the gate-gradient partials
     float* s_part = reinterpret_cast<float*>(smem);
@@ -99,12 +154,21 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       for (int j = 0; j < FN; ++j) {
         const int n = n0 + wn * WN + 16 * j + ncol;
         if (n >= I) continue;
-        const uint2 r1 = *reinterpret_cast<const uint2*>(G13 + (size_t)m * 2 * I + n);
-        const uint2 r3 = *reinterpret_cast<const uint2*>(G13 + (size_t)m * 2 * I + I + n);
-        const float g1v[4] = {__uint_as_float(r1.x << 16), __uint_as_float(r1.x & 0xFFFF0000u),
-                              __uint_as_float(r1.y << 16), __uint_as_float(r1.y & 0xFFFF0000u)};
-        const float g3v[4] = {__uint_as_float(r3.x << 16), __uint_as_float(r3.x & 0xFFFF0000u),
-                              __uint_as_float(r3.y << 16), __uint_as_float(r3.y & 0xFFFF0000u)};
+        const size_t o1 = (size_t)m * 2 * I + n, o3 = o1 + I;
+        float g1v[4], g3v[4];
+        if constexpr (F32IO) {
+          const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.G13) + o1);
+          const f32x4_t r3 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.G13) + o3);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) { g1v[v] = r1[v]; g3v[v] = r3[v]; }
+        } else {
+          const uint2 r1 = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(a.G13) + o1);
+          const uint2 r3 = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(a.G13) + o3);
+          g1v[0] = __uint_as_float(r1.x << 16); g1v[1] = __uint_as_float(r1.x & 0xFFFF0000u);
+          g1v[2] = __uint_as_float(r1.y << 16); g1v[3] = __uint_as_float(r1.y & 0xFFFF0000u);
+          g3v[0] = __uint_as_float(r3.x << 16); g3v[1] = __uint_as_float(r3.x & 0xFFFF0000u);
+          g3v[2] = __uint_as_float(r3.y << 16); g3v[3] = __uint_as_float(r3.y & 0xFFFF0000u);
+        }
         float d1[4], d3[4], ag[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -118,9 +182,17 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
           d3[v] = da * silu;
           ag[v] = g * av;
         }
-        *reinterpret_cast<uint2*>(dG13 + (size_t)m * 2 * I + n) = pack4(d1[0], d1[1], d1[2], d1[3]);
-        *reinterpret_cast<uint2*>(dG13 + (size_t)m * 2 * I + I + n) = pack4(d3[0], d3[1], d3[2], d3[3]);
-        *reinterpret_cast<uint2*>(Ag + (size_t)m * I + n) = pack4(ag[0], ag[1], ag[2], ag[3]);
+        if constexpr (F32IO) {
+          float* dG = static_cast<float*>(a.dG13);
+          *reinterpret_cast<f32x4_t*>(dG + o1) = f32x4_t{d1[0], d1[1], d1[2], d1[3]};
+          *reinterpret_cast<f32x4_t*>(dG + o3) = f32x4_t{d3[0], d3[1], d3[2], d3[3]};
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.Ag) + (size_t)m * I + n) = f32x4_t{ag[0], ag[1], ag[2], ag[3]};
+        } else {
+          bf16_t* dG = static_cast<bf16_t*>(a.dG13);
+          *reinterpret_cast<uint2*>(dG + o1) = pack4(d1[0], d1[1], d1[2], d1[3]);
+          *reinterpret_cast<uint2*>(dG + o3) = pack4(d3[0], d3[1], d3[2], d3[3]);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.Ag) + (size_t)m * I + n) = pack4(ag[0], ag[1], ag[2], ag[3]);
+        }
       }
     }
     // lanes sharing a row, then the WGN waves of a row block, in a fixed order

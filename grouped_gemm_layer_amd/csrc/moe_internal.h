@@ -66,10 +66,11 @@ struct LayerArgs {
   const void* w2;                 // [E,H,I]
   const void* dy;                 // [T,H]
   // forward intermediates / outputs
+  int g13_f32;                    // G13 stored in fp32 (fp8_bwd mode) instead of the activation type
   void* G13;                      // [M,2I]  (saved)
   void* A;                        // [M,I]
   void* O;                        // [M,H]
-  // backward intermediates / outputs
+  // backward intermediates / outputs (fp32 in fp8_bwd mode)
   void* dG13;                     // [M,2I]
   void* Ag;                       // [M,I]   gate * A
   void* dXp;                      // [M,H]
@@ -77,6 +78,30 @@ struct LayerArgs {
   float* dw13;                    // [E,2I,H]
   float* dw2;                     // [E,H,I]
 };
+
+// MXFP8 operands of the backward GEMMs (fp8_bwd mode).  Every operand is
+// stored K-contiguous: codes [rows][K] (E4M3FN bytes) and scales [rows][K/32]
+// (E8M0 bytes), K = the GEMM's reduction dimension.  The token-K operands of
+// the weight gradients are transposed copies whose K is the padded token
+// order: expert e's rows start at pad_off[e], a multiple of MX_KTILE, and the
+// gap up to the next expert holds zero codes.
+constexpr int MX_KTILE = 128;   // K elements per tile of the MXFP8 GEMMs (one scaled MFMA step)
+struct Mx8Args {
+  const int32_t* pad_off;       // [E+1] padded token offsets (multiples of MX_KTILE)
+  int Mp;                       // padded token capacity (row length of the token-K operands)
+  const uint8_t *qdy, *sdy;     // [T][H]      dY rows, K = H
+  const uint8_t *qw2t, *sw2t;   // [E][I][H]   W2 transposed, K = H
+  const uint8_t *qdg, *sdg;     // [M][2I]     dG13 rows, K = 2I
+  const uint8_t *qw13t, *sw13t; // [E][H][2I]  W13 transposed, K = 2I
+  const uint8_t *qdyt, *sdyt;   // [H][Mp]     gathered dY, K = tokens
+  const uint8_t *qagt, *sagt;   // [I][Mp]     gate * A, K = tokens
+  const uint8_t *qdgt, *sdgt;   // [2I][Mp]    dG13, K = tokens
+  const uint8_t *qxt, *sxt;     // [H][Mp]     gathered x, K = tokens
+};
+// Padded token capacity: every expert rounds its count up to MX_KTILE.
+inline size_t mx_token_capacity(size_t M, int E) {
+  return (M + MX_KTILE - 1) / MX_KTILE * MX_KTILE + (size_t)E * MX_KTILE;
+}
 
 // Number of M tiles of height bm over all experts is at most this bound.
 inline int max_row_tiles(int M, int E, int bm) { return (M + bm - 1) / bm + E; }
@@ -116,15 +141,42 @@ hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s);
 hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s);
 
+// MXFP8 backward GEMMs (kind = KIND_DGRAD2 .. KIND_WGRAD1)
+hipError_t launch_gemm_mx8(GemmKind kind, const LayerArgs& a, const Mx8Args& q, hipStream_t s);
+int mx8_row_tile_m();       // token rows per tile of the row-ragged MXFP8 GEMMs
+int mx8_dgrad2_tile_n();    // columns per tile of the MXFP8 dgrad of W2
+
+// MXFP8 quantisers (E4M3FN codes + E8M0 scales per 32 elements, round to
+// nearest even, saturating).  Layouts as in Mx8Args.
+//   rows:      src [R][K] (row src_row(r) = s2f ? s2f[r]/k : r) -> codes [R][K], scales [R][K/32]
+//   cols_t:    per expert, src [Kd][N] -> codes [N][Kd], scales [N][Kd/32]   (Kd % MX_KTILE == 0)
+//   tokens_t:  src rows r of the expert-sorted order (gathered as above) of a
+//              [.][F] matrix -> codes [F][Mp], scales [F][Mp/32], expert e's
+//              rows at pad_off[e] .. (zero-padded to the next multiple of MX_KTILE)
+template <typename T>   // T = bf16_t or float
+hipError_t launch_mx_quant_rows(const T* src, int R, int K, const int32_t* s2f, int k, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t s);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t s);
+template <typename T>   // T = bf16_t or float
+hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,
+                                    const int32_t* pad_off, int E, int Mp, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t s);
+
 // tiling the API layer needs for workspace sizing and the tile table
 int bf16_row_tile_m();      // token rows per tile of the row-ragged bf16 GEMMs
 int bf16_dgrad2_tile_n();   // columns per tile of the bf16 dgrad of W2
 constexpr int FP32_BM = 64;
 constexpr int FP32_BN = 64;
-inline int row_tile_m(bool bf16) { return bf16 ? bf16_row_tile_m() : FP32_BM; }
-inline int dgrad2_parts(bool bf16, int I) {
+// mode: 0 fp32, 1 bf16, 3 fp8_bwd (the public moe_mode values)
+inline int fwd_row_tile_m(int mode) { return mode == 0 ? FP32_BM : bf16_row_tile_m(); }
+inline int bwd_row_tile_m(int mode) {
+  return mode == 0 ? FP32_BM : mode == 3 ? mx8_row_tile_m() : bf16_row_tile_m();
+}
+inline int dgrad2_parts(int mode, int I) {
   // N tiles of the dgrad of W2 (N = I): one gate-gradient partial per tile
-  const int bn = bf16 ? bf16_dgrad2_tile_n() : FP32_BN;
+  const int bn = mode == 0 ? FP32_BN : mode == 3 ? mx8_dgrad2_tile_n() : bf16_dgrad2_tile_n();
   return (I + bn - 1) / bn;
 }
 

@@ -36,7 +36,9 @@
  *   w2 [E,H,I];  logits [T,E] fp32;  dw13 [E,2I,H] fp32;  dw2 [E,H,I] fp32.
  * Element type of x/dy/y/dx/w13/w2: fp32 in MOE_MODE_FP32, bf16 (raw 16-bit
  * patterns) otherwise.  Gates, gate/logit gradients and weight gradients are
- * always fp32.  Current limits: H and I multiples of 64, E <= 512, k <= 32.
+ * always fp32.  Current limits: H and I multiples of 64 (H a multiple of 128
+ * in MOE_MODE_FP8_BWD), E <= 512, k <= 32, and every activation-sized buffer
+ * below 2 GiB (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -52,8 +54,8 @@ extern "C" {
 typedef enum {
   MOE_MODE_FP32 = 0,     /* fp32 activations/weights (debug and tiny shapes) */
   MOE_MODE_BF16 = 1,     /* bf16 storage, fp32 accumulation, MFMA GEMMs */
-  MOE_MODE_MXFP8 = 2,    /* reserved: MXFP8 forward and backward (not yet built) */
-  MOE_MODE_FP8_BWD = 3   /* bf16 forward, MXFP8 backward (not yet built) */
+  MOE_MODE_MXFP8 = 2,    /* reserved: MXFP8 forward and backward (not built; MOE_ERR_UNSUPPORTED) */
+  MOE_MODE_FP8_BWD = 3   /* bf16 forward, MXFP8 backward GEMMs (see moe_backward) */
 } moe_mode;
 
 typedef enum {
@@ -122,7 +124,19 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, con
  *   dlogits[t,e] = gate_e (dgate_e - sum_j gate_j dgate_j) on the top-k set, else 0
  * dy, x, w13, w2: device inputs; saved: from moe_forward; dx: device [T,H];
  * dw13, dw2: device fp32, overwritten; dgate: device [T,k] fp32; dlogits:
- * device [T,E] fp32 or NULL to skip. */
+ * device [T,E] fp32 or NULL to skip.
+ *
+ * MOE_MODE_FP8_BWD (Prime Mega MoE news page, "How does the fused kernel
+ * work?": BF16 forward with FP8 backward; TE dropless-MoE page, "03
+ * Specialised optimisations": group-aware MXFP8 quantisation and MXFP8
+ * grouped GEMM): the four GEMMs above read both operands as MXFP8, each
+ * quantised along that GEMM's reduction dimension as moe_mxfp8_quantize
+ * describes: dy and W2 along H, dG13 and W13 along 2I, and for the weight
+ * gradients dy, gate*A, dG13 and x along the tokens of each expert in blocks
+ * that start at the expert's first row (moe_mxfp8_quantize_grouped).  The
+ * quantisers see fp32 values of dG13 and gate*A (in this mode the forward
+ * saves G13 in fp32); dgate, the SwiGLU derivative and the router gradient
+ * use the unquantised forward state. */
 moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, const void* w13,
                         const void* w2, const moe_routing* routing, const void* saved,
                         void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
@@ -136,7 +150,12 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  * (MOE_ERR_NULL / MOE_ERR_DIMS otherwise).  Kernel order:
  *   forward : tile table, GEMM W13 + SwiGLU, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
- *             unpermute-reduce, router backward, wgrad W2, wgrad W13 */
+ *             unpermute-reduce, router backward, wgrad W2, wgrad W13
+ *   backward, MOE_MODE_FP8_BWD: tile table, quantise W2^T, quantise dy,
+ *             dgrad W2 + SwiGLU derivative, quantise W13^T, quantise dG13,
+ *             dgrad W13, unpermute-reduce, router backward, padded expert
+ *             offsets, quantise dy^T, quantise (gate*A)^T, wgrad W2,
+ *             quantise dG13^T, quantise x^T, wgrad W13 */
 moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                              const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events, int n_events);
@@ -145,9 +164,44 @@ moe_status moe_backward_timed(const moe_dims* dims, const void* dy, const void* 
                               float* dw13, float* dw2, float* dgate, float* dlogits, void* ws, size_t ws_bytes,
                               hipStream_t stream, hipEvent_t* events, int n_events);
 
-/* Number of kernels a call launches: which = 0 route, 1 forward, 2 backward
- * (-1 for any other value).  Host-only. */
-int moe_num_kernels(int which);
+/* Number of kernels a call with these dims launches: which = 0 route,
+ * 1 forward, 2 backward (-1 for any other value or invalid dims).  Host-only. */
+int moe_num_kernels(const moe_dims* dims, int which);
+
+/* MXFP8 quantisation of a bf16 matrix (OCP microscaling format as the TE
+ * dropless-MoE page, "03 Specialised optimisations", applies it: E4M3FN
+ * elements with one E8M0 scale per 32 consecutive elements along the GEMM's
+ * reduction dimension).  For a block with largest magnitude amax:
+ *   X     = the smallest integer with amax <= 448 * 2^X, clamped to [-127, 127]
+ *           (-127 for an all-zero block); scale byte = X + 127;
+ *   codes = v / 2^X rounded to the nearest E4M3FN value, ties to the even
+ *           code, magnitudes above 448 saturate to 448; the sign bit of v is
+ *           kept, also when the value rounds to zero.
+ * src: device bf16 [rows, cols] row-major.
+ *   along = 1: blocks of 32 along each row (cols % 32 == 0):
+ *              codes [rows, cols], scales [rows, cols/32];
+ *   along = 0: blocks of 32 down each column (rows % 128 == 0), written
+ *              transposed: codes [cols, rows], scales [cols, rows/32].
+ * codes, scales: device outputs (bytes), 256-byte aligned.  Deterministic;
+ * the codes are those of the exact definition for the given bf16 values. */
+moe_status moe_mxfp8_quantize(const void* src, int32_t rows, int32_t cols, int32_t along, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
+
+/* Group-aware MXFP8 quantisation along the rows of expert-sorted data (TE
+ * dropless-MoE page, "03 Specialised optimisations"): src: device bf16
+ * [rows, cols] whose rows offsets[e] .. offsets[e+1]-1 belong to expert e
+ * (offsets: device int32 [E+1], offsets[0] = 0, offsets[E] = rows).  Blocks
+ * of 32 rows start at each expert's first row; an expert's last block is
+ * zero-padded.  Output, transposed and padded: expert e's rows occupy
+ * columns pad_off[e] .. of codes [cols, capacity] and scales
+ * [cols, capacity/32], pad_off[e] = sum over e' < e of the counts rounded up
+ * to 128 (pad_off: device int32 [E+1], written); columns from
+ * pad_off[e] + count_e up to pad_off[e+1] hold zero codes.  capacity must be
+ * a multiple of 128 and at least moe_mxfp8_grouped_capacity(rows, E). */
+moe_status moe_mxfp8_quantize_grouped(const void* src, int32_t rows, int32_t cols, const int32_t* offsets,
+                                      int32_t E, int32_t capacity, int32_t* pad_off, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t stream);
+size_t moe_mxfp8_grouped_capacity(int32_t rows, int32_t E);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status status);

@@ -114,3 +114,45 @@ def oracle_expert_wgrad(orc, inp: dict, r, e: int) -> dict:
     f = orc.expert_forward(inp["x"][tok], w13[e], w2[e])
     bw = orc.expert_backward(g[:, None] * inp["dy"][tok].astype(np.float64), inp["x"][tok], w13[e], w2[e], f)
     return {"dw13": bw["dW13"], "dw2": bw["dW2"]}
+
+
+def oracle_token_rows_mx8(orc, inp: dict, r, tokens) -> dict:
+    """dX, dgate, dlogits of the given tokens under the fp8_bwd backward.
+
+    Row-wise quantisation (along H and 2I) treats each row on its own, so the
+    rows of the sampled tokens are evaluated expert by expert with the
+    oracle's per-expert fp8_bwd function (its weight gradients, which depend
+    on all rows of the expert, are not used here)."""
+    k = r.k
+    x, w13, w2, dy = inp["x"], inp["w13"], inp["w2"], inp["dy"]
+    H = x.shape[1]
+    dX = np.zeros((len(tokens), H))
+    dgate = np.zeros((len(tokens), k))
+    by_e = {}
+    for a, t in enumerate(tokens):
+        for j in range(k):
+            by_e.setdefault(int(r.idx[t, j]), []).append((a, int(t), j))
+    for e, rows in by_e.items():
+        toks = np.array([t for _, t, _ in rows])
+        g = np.array([r.gate[t, j] for _, t, j in rows])
+        f = orc.expert_forward(x[toks], w13[e], w2[e])
+        out = orc.expert_backward_mxfp8(dy[toks], x[toks], g, w13[e], w2[e], f)
+        for i, (a, t, j) in enumerate(rows):
+            dX[a] += out["dXp"][i]
+            dgate[a, j] = out["dgate"][i]
+    dlog = orc.router_backward(r.gate[tokens], dgate, r.idx[tokens], r.E)
+    return {"dx": dX, "dgate": dgate, "dlogits": dlog}
+
+
+def oracle_expert_wgrad_mx8(orc, inp: dict, r, e: int) -> dict:
+    """Weight gradients of expert e under the fp8_bwd backward (all of its rows)."""
+    a, b = int(r.offsets[e]), int(r.offsets[e + 1])
+    w13, w2 = inp["w13"], inp["w2"]
+    if b == a:
+        return {"dw13": np.zeros(w13.shape[1:]), "dw2": np.zeros(w2.shape[1:])}
+    flat = r.sorted_to_flat[a:b]
+    tok = flat // r.k
+    g = r.gate.reshape(-1)[flat]
+    f = orc.expert_forward(inp["x"][tok], w13[e], w2[e])
+    out = orc.expert_backward_mxfp8(inp["dy"][tok], inp["x"][tok], g, w13[e], w2[e], f)
+    return {"dw13": out["dW13"], "dw2": out["dW2"]}

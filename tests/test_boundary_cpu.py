@@ -53,6 +53,7 @@ def test_workspace_sizes_scale():
     ((0, 128, 64, 8, 2, 1), 2), ((16, 128, 64, 8, 9, 1), 2), ((16, -1, 64, 8, 2, 1), 2),
     ((16, 100, 64, 8, 2, 1), 3), ((16, 128, 96, 8, 2, 1), 3), ((16, 128, 64, 8, 2, 2), 3),
     ((16, 128, 64, 1024, 2, 1), 3), ((16, 128, 64, 64, 33, 1), 3), ((16, 128, 64, 8, 2, 7), 3),
+    ((16, 192, 64, 8, 2, 3), 3), ((1 << 20, 4096, 1536, 128, 8, 1), 3),
 ])
 def test_invalid_dims(dims, status):
     g, lib = _lib()
@@ -118,10 +119,56 @@ def test_forward_backward_argument_errors():
         g.backward(d, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), _FakeTensor(0x7C0000000010), t(8), None,
                    t(9), stream=_NullStream())
     assert ei.value.status == 4
-    dbad = g.Dims.of(64, 128, 64, 8, 2, "fp8_bwd")
-    with pytest.raises(g.MoeError) as ei:
-        g.forward(dbad, t(0), t(1), t(2), r, t(3), t(4), t(5), stream=_NullStream())
-    assert ei.value.status == 3
+    for dbad in (g.Dims.of(64, 128, 64, 8, 2, "mxfp8"), g.Dims.of(64, 192, 64, 8, 2, "fp8_bwd")):
+        with pytest.raises(g.MoeError) as ei:
+            g.forward(dbad, t(0), t(1), t(2), r, t(3), t(4), t(5), stream=_NullStream())
+        assert ei.value.status == 3
+        with pytest.raises(g.MoeError) as ei:
+            g.backward(dbad, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), t(7), t(8), None, t(9),
+                       stream=_NullStream())
+        assert ei.value.status == 3
+
+
+def test_num_kernels_by_mode():
+    g, lib = _lib()
+    bf = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    f8 = g.Dims.of(64, 128, 64, 8, 2, "fp8_bwd")
+    assert g.num_kernels(bf, "route") == 4 and g.num_kernels(bf, "forward") == 4
+    assert g.num_kernels(bf, "backward") == 7
+    assert g.num_kernels(f8, "forward") == 4 and g.num_kernels(f8, "backward") == 16
+    assert lib.moe_num_kernels(ctypes.byref(g.Dims.of(0, 128, 64, 8, 2, "bf16")), 1) == -1
+    assert lib.moe_num_kernels(ctypes.byref(bf), 7) == -1
+
+
+def test_fp8_bwd_workspace_holds_quantised_operands():
+    g, lib = _lib()
+    T, H, I, E, k = 16384, 2048, 768, 128, 8
+    bws_bf16 = g.workspace_size(g.Dims.of(T, H, I, E, k, "bf16"))[3]
+    rws, saved, fws, bws = g.workspace_size(g.Dims.of(T, H, I, E, k, "fp8_bwd"))
+    M = T * k
+    Mp = g.mxfp8_grouped_capacity(M, E)
+    assert Mp % 128 == 0 and Mp >= M + 127 * E
+    codes = T * H + E * 3 * I * H + M * 2 * I + Mp * (2 * H + 3 * I)
+    assert bws >= bws_bf16 - M * 4 * 6 + codes * 33 // 32
+
+
+def test_mxfp8_quantize_argument_errors():
+    g, lib = _lib()
+    t = lambda i: _FakeTensor(0x7C0000000000 + i * 0x1000000)
+    q = lib.moe_mxfp8_quantize
+    assert q(None, 64, 64, 1, t(1).addr, t(2).addr, None) == 1
+    assert q(t(0).addr, 0, 64, 1, t(1).addr, t(2).addr, None) == 2
+    assert q(t(0).addr, 64, 64, 2, t(1).addr, t(2).addr, None) == 2
+    assert q(t(0).addr, 64, 48, 1, t(1).addr, t(2).addr, None) == 3      # cols % 32
+    assert q(t(0).addr, 64, 64, 0, t(1).addr, t(2).addr, None) == 3      # rows % 128 when along = 0
+    assert q(t(0).addr + 16, 64, 64, 1, t(1).addr, t(2).addr, None) == 4
+    qg = lib.moe_mxfp8_quantize_grouped
+    cap = g.mxfp8_grouped_capacity(100, 4)
+    assert cap == 128 + 4 * 128
+    assert qg(t(0).addr, 100, 64, t(1).addr, 4, cap, None, t(3).addr, t(4).addr, None) == 1
+    assert qg(t(0).addr, 100, 64, t(1).addr, 4, cap - 128, t(2).addr, t(3).addr, t(4).addr, None) == 3
+    assert qg(t(0).addr, 100, 64, t(1).addr, 4, cap + 32, t(2).addr, t(3).addr, t(4).addr, None) == 3
+    assert qg(t(0).addr, 100, 64, t(1).addr + 4, 4, cap, t(2).addr, t(3).addr, t(4).addr, None) == 4
 
 
 class _NullStream:
