@@ -1,6 +1,6 @@
 """Benchmark of the MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--cpu-tokens 4096] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--cpu-tokens 8192] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 route + forward + backward of the layer (Qwen3-30B-A3B expert shape by
@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
     args = ap.parse_args()

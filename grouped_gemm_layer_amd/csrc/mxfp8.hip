@@ -13,40 +13,34 @@
 // the next multiple of MX_KTILE where the next expert starts.
 //
 // Layouts written here (bytes): codes [rows][K], scales [rows][K/32], K the
-// operand's GEMM-K (contiguous).  The scaling by 2^-X and the rounding are
-// exact in fp32, so the codes equal those of the exact definition for the
-// same bf16 inputs.
+// operand's GEMM-K (contiguous).  The scaling by 2^-X is exact (ldexp) and the
+// E4M3 rounding is the hardware conversion (nearest, ties to even), so the
+// codes are those of the exact definition for the same inputs.
 #include "moe_internal.h"
 
 namespace moe {
 
+// X from the bits of amax (finite, >= 0): amax = (1 + f) 2^(eb-127) and
+// 448 = 1.75 * 2^8, so X = eb - 135 when f <= 0.75, else eb - 134.
 __device__ __forceinline__ int mx_scale_exp(float amax) {
-  if (!(amax > 0.f)) return -127;
-  int ea;
-  const float m = frexpf(amax, &ea);   // amax = m 2^ea, m in [0.5, 1)
-  // amax = (2m) 2^(ea-1); 448 = 1.75 2^8
-  const int X = (2.f * m <= 1.75f) ? ea - 9 : ea - 8;
+  const uint32_t b = __float_as_uint(amax);
+  const int eb = (int)(b >> 23);
+  int X;
+  if (eb != 0) {
+    X = eb - 127 - ((b & 0x7FFFFFu) <= 0x600000u ? 8 : 7);
+  } else {                              // zero or an fp32 subnormal
+    if (b == 0) return -127;
+    int ea;
+    const float m = frexpf(amax, &ea);  // amax = m 2^ea, m in [0.5, 1)
+    X = (2.f * m <= 1.75f) ? ea - 9 : ea - 8;
+  }
   return min(max(X, -127), 127);
 }
 
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {                 // below 2^-6: subnormal grid m 2^-9, m = 0..8
-    code = (uint32_t)rintf(a * 512.f); // m = 8 is 2^-6, the smallest normal (code 0x08)
-  } else {
-    int e;
-    (void)frexpf(a, &e);
-    int E = e - 1;                     // a in [2^E, 2^(E+1)), E >= -6
-    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - E));   // 8..16, exact scaling, ties to even
-    if (q == 16u) { q = 8u; E += 1; }
-    code = min(((uint32_t)(E + 7) << 3) | (q - 8u), 0x7Eu);
-  }
-  return code | sign;
-}
-
-// 32 values -> 32 codes packed into 8 words, returns the E8M0 byte.
+// 32 values -> 32 codes packed into 8 words (element i in byte i%4 of word
+// i/4), returns the E8M0 byte.  v / 2^X is exact (ldexp); the hardware
+// conversion rounds to the nearest E4M3FN value, ties to even, and keeps the
+// sign of zero; |v / 2^X| <= 448 by the choice of X, so nothing overflows.
 __device__ __forceinline__ uint32_t mx_quant_block(const float (&v)[32], uint32_t (&packed)[8]) {
   float amax = 0.f;
 #pragma unroll
@@ -54,10 +48,9 @@ __device__ __forceinline__ uint32_t mx_quant_block(const float (&v)[32], uint32_
   const int X = mx_scale_exp(amax);
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_encode(ldexpf(v[4 * w + b], -X)) << (8 * b);
-    packed[w] = word;
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w], -X), ldexpf(v[4 * w + 1], -X), 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w + 2], -X), ldexpf(v[4 * w + 3], -X), word, true);
+    packed[w] = (uint32_t)word;
   }
   return (uint32_t)(X + 127);
 }
@@ -109,32 +102,6 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const T* __restrict_
   }
 }
 
-// Column blocks, per expert: source S[e] is [Kd][N] (K outer); output codes
-// [e][N][Kd] (K contiguous) and scales [e][N][Kd/32].  Thread = one column n
-// and MX_KTILE consecutive k (4 blocks): the loads of one source row are
-// contiguous across the threads, each thread stores one 128-byte line.
-__global__ __launch_bounds__(256) void mx_quant_cols_t_kernel(const bf16_t* __restrict__ src, int Kd, int N,
-                                                              uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int c = blockIdx.y, e = blockIdx.z;
-  if (n >= N) return;
-  const bf16_t* s = src + (size_t)e * Kd * N + (size_t)(MX_KTILE * c) * N + n;
-  uint4* o = reinterpret_cast<uint4*>(codes + ((size_t)e * N + n) * Kd + MX_KTILE * c);
-  uint32_t sc4 = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(s[(size_t)(32 * q + i) * N]);
-    uint32_t packed[8];
-    sc4 |= mx_quant_block(v, packed) << (8 * q);
-    o[2 * q] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    o[2 * q + 1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  }
-  *reinterpret_cast<uint32_t*>(scales + ((size_t)e * N + n) * (Kd / 32) + 4 * c) = sc4;
-}
-
 // Padded token offsets: pad_off[e] = sum_{e' < e} ceil(count_e' / MX_KTILE) * MX_KTILE.
 __global__ __launch_bounds__(512) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int32_t* __restrict__ pad_off) {
@@ -155,50 +122,101 @@ __global__ __launch_bounds__(512) void pad_offsets_kernel(const int32_t* __restr
   if (e == 0) pad_off[0] = 0;
 }
 
-// Token blocks, transposed: source rows r (expert-sorted order) of a [.][F]
-// matrix, read as src[s2f[r] / k] when s2f is given (gathered x / dY rows);
-// output codes [F][Mp] and scales [F][Mp/32].  Block = one padded tile of
-// MX_KTILE tokens (inside a single expert's padded range) x 256 features;
-// thread = one feature, 4 blocks of 32 tokens, one 128-byte line of codes.
-template <typename T>
-__global__ __launch_bounds__(256) void mx_quant_tokens_t_kernel(const T* __restrict__ src, int F,
-                                                                const int32_t* __restrict__ s2f, int k,
-                                                                const int32_t* __restrict__ offsets,
-                                                                const int32_t* __restrict__ pad_off, int E,
-                                                                int Mp, uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scales) {
-  __shared__ int s_src[MX_KTILE];       // source row of each token of the tile, -1 = padding
+// Transposing quantiser: blocks of 32 run down the rows of the source and
+// the output is written transposed (feature-major), K = the source's rows.
+//   GROUPED: source rows r of the expert-sorted order (read as
+//     src[s2f[r] / k] when s2f is given: gathered x / dY rows); expert e's
+//     rows go to output columns pad_off[e] .., the gap up to pad_off[e+1]
+//     holds zero codes; grid.y = padded tiles of MX_KTILE columns.
+//   dense: blockIdx.z = expert of a [E][Kd][F] source, rows e*Kd + p;
+//     output [E][F][Kd]; grid.y = Kd / MX_KTILE.
+// A tile of MX_KTILE rows x QT_F features is staged in LDS as fp32 with
+// coalesced 16-byte row loads; thread (f, q) then quantises feature f over
+// the 32 rows of block q and stores its 32 codes and one scale byte.
+constexpr int QT_F = 64;            // features per tile
+constexpr int QT_LD = QT_F + 4;     // LDS row stride (floats): rows stay 16-byte aligned
+
+template <typename T, bool GROUPED>
+__global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ src, int F,
+                                                         const int32_t* __restrict__ s2f, int k,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ pad_off, int E, int Kd,
+                                                         int ld_out, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) float s_tile[MX_KTILE * QT_LD];
+  __shared__ int s_src[MX_KTILE];       // source row of each tile row, -1 = padding
+  const int f0 = blockIdx.x * QT_F;
   const int p0 = MX_KTILE * blockIdx.y;
-  if (p0 >= pad_off[E]) return;         // uniform over the block
-  int lo = 0, hi = E - 1;               // expert e with pad_off[e] <= p0 < pad_off[e+1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pad_off[mid] <= p0) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  if (threadIdx.x < MX_KTILE) {
-    const int r = offsets[e] + (p0 - pad_off[e]) + threadIdx.x;
-    s_src[threadIdx.x] = (r < offsets[e + 1]) ? (s2f ? s2f[r] / k : r) : -1;
+  size_t out_base = 0, sc_base = 0;
+  if constexpr (GROUPED) {
+    if (p0 >= pad_off[E]) return;       // uniform over the block
+    int lo = 0, hi = E - 1;             // expert e with pad_off[e] <= p0 < pad_off[e+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pad_off[mid] <= p0) lo = mid; else hi = mid - 1;
+    }
+    if (threadIdx.x < MX_KTILE) {
+      const int r = offsets[lo] + (p0 - pad_off[lo]) + threadIdx.x;
+      s_src[threadIdx.x] = (r < offsets[lo + 1]) ? (s2f ? s2f[r] / k : r) : -1;
+    }
+  } else {
+    const int e = blockIdx.z;
+    if (threadIdx.x < MX_KTILE) s_src[threadIdx.x] = e * Kd + p0 + threadIdx.x;
+    out_base = (size_t)e * F * ld_out;
+    sc_base = (size_t)e * F * (ld_out / 32);
   }
   __syncthreads();
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
-  uint4* o = reinterpret_cast<uint4*>(codes + (size_t)f * Mp + p0);
-  uint32_t sc4 = 0;
+
+  // rows -> LDS: every load of the thread is issued before the first store
+  constexpr int EPC = 16 / (int)sizeof(T);      // values per 16-byte chunk
+  constexpr int CPR = QT_F / EPC;               // chunks per tile row
+  constexpr int RPP = 256 / CPR;                // tile rows per pass
+  constexpr int NP = MX_KTILE / RPP;            // passes
+  const int c = threadIdx.x % CPR, fc = f0 + c * EPC, r0 = threadIdx.x / CPR;
+  if ((F % EPC) == 0) {                         // rows 16-byte aligned, chunks never straddle F
+    uint4 raw[NP];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float v[32];
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int sr = s_src[32 * q + t];
-      v[t] = (sr >= 0) ? ElemTraits<T>::load(src + (size_t)sr * F + f) : 0.f;
+    for (int p = 0; p < NP; ++p) {
+      const int sr = s_src[r0 + p * RPP];
+      raw[p] = (sr >= 0 && fc < F) ? *reinterpret_cast<const uint4*>(src + (size_t)sr * F + fc)
+                                   : make_uint4(0u, 0u, 0u, 0u);
     }
-    uint32_t packed[8];
-    sc4 |= mx_quant_block(v, packed) << (8 * q);
-    o[2 * q] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    o[2 * q + 1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      float v[EPC];
+      if constexpr (sizeof(T) == 2) {
+        unpack_bf16x8(raw[p], v);
+      } else {
+        v[0] = __uint_as_float(raw[p].x); v[1] = __uint_as_float(raw[p].y);
+        v[2] = __uint_as_float(raw[p].z); v[3] = __uint_as_float(raw[p].w);
+      }
+      float* d = &s_tile[(r0 + p * RPP) * QT_LD + c * EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) *reinterpret_cast<f32x4_t*>(d + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    }
+  } else {
+    for (int r = r0; r < MX_KTILE; r += RPP) {
+      const int sr = s_src[r];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i)
+        s_tile[r * QT_LD + c * EPC + i] =
+            (sr >= 0 && fc + i < F) ? ElemTraits<T>::load(src + (size_t)sr * F + fc + i) : 0.f;
+    }
   }
-  *reinterpret_cast<uint32_t*>(scales + (size_t)f * (Mp / 32) + p0 / 32) = sc4;
+  __syncthreads();
+
+  // one feature x one block of 32 rows per thread (a wave = 64 features of one block)
+  const int f = threadIdx.x % QT_F, q = threadIdx.x / QT_F;
+  if (f0 + f >= F) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = s_tile[(32 * q + i) * QT_LD + f];
+  uint32_t packed[8];
+  const uint32_t sc = mx_quant_block(v, packed);
+  uint4* o = reinterpret_cast<uint4*>(codes + out_base + (size_t)(f0 + f) * ld_out + p0 + 32 * q);
+  o[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  o[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  scales[sc_base + (size_t)(f0 + f) * (ld_out / 32) + p0 / 32 + q] = (uint8_t)sc;
 }
 
 template <typename T>
@@ -216,8 +234,8 @@ template hipError_t launch_mx_quant_rows<float>(const float*, int, int, const in
 
 hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(mx_quant_cols_t_kernel, dim3((N + 255) / 256, Kd / MX_KTILE, E), dim3(256), 0, s, src, Kd, N,
-                     codes, scales);
+  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false>), dim3((N + QT_F - 1) / QT_F, Kd / MX_KTILE, E), dim3(256),
+                     0, s, src, N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes, scales);
   return hipGetLastError();
 }
 
@@ -230,8 +248,8 @@ template <typename T>
 hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,
                                     const int32_t* pad_off, int E, int Mp, uint8_t* codes, uint8_t* scales,
                                     hipStream_t s) {
-  hipLaunchKernelGGL(mx_quant_tokens_t_kernel<T>, dim3((F + 255) / 256, Mp / MX_KTILE), dim3(256), 0, s, src, F,
-                     s2f, k, offsets, pad_off, E, Mp, codes, scales);
+  hipLaunchKernelGGL((mx_quant_t_kernel<T, true>), dim3((F + QT_F - 1) / QT_F, Mp / MX_KTILE), dim3(256), 0, s,
+                     src, F, s2f, k, offsets, pad_off, E, 0, Mp, codes, scales);
   return hipGetLastError();
 }
 template hipError_t launch_mx_quant_tokens_t<bf16_t>(const bf16_t*, int, const int32_t*, int, const int32_t*,

@@ -19,8 +19,9 @@ within the quantised oracle's own error plus the bound against it.
 
 The bounds against the quantised oracle: both sides quantise the same bf16
 inputs bit-exactly, and dG13 and gate*A enter the quantisers in fp32 on the
-GPU and in fp64 in the oracle.  gate*A comes from the forward state alone, so
-dgate, dlogits and dW2 agree to ~1e-4.  dG13 also contains dA' from the
+GPU and in fp64 in the oracle.  gate*A comes from the forward state alone
+(fp32 accumulations of the bf16 forward GEMMs, ~1e-6 relative), so its
+codes flip only rarely: dgate and dlogits agree to ~1e-4, dW2 to a few 1e-3.  dG13 also contains dA' from the
 scaled-MFMA dgrad of W2, whose internal accumulation keeps about 1e-5 of the
 sum of |products| per instruction (measured on the device against an exact
 product), i.e. ~2e-4 of a typical dA' value at K = H.  Where that moves a dG13
@@ -40,7 +41,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_EXACT = 6e-2      # MXFP8 backward gradients against the exact fp64 backward
 # against the fp64 oracle of the quantised backward (per output; see above)
-TOL_QORACLE = {"dx": 4e-2, "dw13": 4e-2, "dw2": 2e-3, "dgate": 2e-3, "dlogits": 2e-3}
+TOL_QORACLE = {"dx": 4e-2, "dw13": 4e-2, "dw2": 1e-2, "dgate": 2e-3, "dlogits": 2e-3}
 TOL_FWD = 2e-2        # the bf16 forward
 
 
