@@ -1,6 +1,6 @@
 """Benchmark of the MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--cpu-tokens 8192] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--cpu-tokens 16384] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 route + forward + backward of the layer (Qwen3-30B-A3B expert shape by
@@ -15,6 +15,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -76,6 +78,52 @@ def hbm_bytes(d):
             "quant_xt": q(M * H)}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's kernel sources and headers: recorded counter
+    figures apply only while this is unchanged."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "grouped_gemm_layer_amd", "csrc", "*"))
+                   + [os.path.join(ROOT, "include", "moe.h"),
+                      os.path.join(ROOT, "grouped_gemm_layer_amd", "build_lib.py")])
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: int, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC figures
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
+    they are missing or were taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash() or rec.get("config") != config:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def copy_calibration(mib: int):
+    """One plain device-to-device copy of `mib` MiB (bytes known exactly), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def cpu_baseline(d, inp, n_tokens):
     """The fp64 oracle on the first n_tokens tokens of the same batch (all experts)."""
     import numpy as np
@@ -104,9 +152,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB before the timed region (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -129,6 +179,8 @@ def main():
     x, w13, w2, dy = dev(inp["x"], adt), dev(inp["w13"], adt), dev(inp["w2"], adt), dev(inp["dy"], adt)
     logits = dev(inp["logits"], torch.float32)
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
 
     ev = HipEvents()
     nf, nb = g.num_kernels(layer.dims, "forward"), g.num_kernels(layer.dims, "backward")
@@ -194,7 +246,8 @@ def main():
     dom = max(flops, key=lambda n: avg[n])
     dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2), "peak": peak[dom],
-                "unit": "TFLOP/s", "frac": round(dom_tf / peak[dom], 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(dom_tf / peak[dom], 4),
+                "traffic": recorded_traffic(args.config, dom),
                 "flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
     gemm_ms = sum(avg[n] for n in flops)
     out = {
