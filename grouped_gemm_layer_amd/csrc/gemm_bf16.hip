@@ -30,11 +30,13 @@
 // (rows m): lane l holds D[n = 4*(l/16) + v][m = l%16], i.e. four consecutive
 // output features of one row, stored as one 8- or 16-byte write.
 //
-// Global loads are raw buffer loads (16 bytes per lane): an offset past the
-// buffer's end returns zeros, which pads the ragged K tail of the wgrad GEMMs
-// without branches.  Pipeline: global -> registers two K tiles ahead (two
-// register sets), LDS double buffer, one barrier per K tile; the token offsets
-// of the gathered wgrad rows come from an LDS table refilled every 2048 rows.
+// Operands travel by buffer-to-LDS DMA (16 bytes per lane, 1 KiB per
+// instruction): an offset past the buffer's end stores zeros, which pads the
+// ragged K tail of the wgrad GEMMs without branches.  Pipeline: STAGES LDS
+// stages; per K tile every wave reads its MFMA fragments into registers
+// between two barriers, then the DMA instructions of the tile STAGES ahead are
+// issued one by one between its MFMAs.  The token offsets of the gathered
+// wgrad rows come from an LDS table refilled every 2048 rows.
 // Blocks are renumbered so that each XCD (8 per chip, blocks dealt
 // round-robin) receives a contiguous range of the expert-major tile order and
 // its L2 serves the shared weight and token panels.
@@ -53,6 +55,7 @@ using gg::OOB;
 using gg::make_rsrc;
 using gg::dma16;
 using gg::vm_wait;
+using gg::u32x4_t;
 
 // ---- LDS layouts (element offsets) ----
 // KC: [row][BK], 16-byte chunk c of row r stored at chunk c ^ swz(r).  With
@@ -250,44 +253,53 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   };
 
   const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)smem;
-  // issue the DMA of K tile kt into stage st (tiles past the end read zeros)
-  auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
+  // DMA instruction q (< DA + DB) of K tile kt into stage st (tiles past the
+  // end read zeros): q < DA fills A-tile block q * NW + w, the rest B-tile blocks
+  auto src_off = [&](int kt, int q) __attribute__((always_inline)) -> uint32_t {
     const bool live = kt < nk;
-    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
-#pragma unroll
-    for (int i = 0; i < DA; ++i) {
-      uint32_t off;
+    if (q < DA) {
+      const int i = q;
       if constexpr (!K_::a_ko) {
-        off = live ? oa[i] + (uint32_t)kt * (BK * 2) : OOB;
+        return live ? oa[i] + (uint32_t)kt * (BK * 2) : OOB;
       } else {
         const int rr = kt * BK + ka[i];
         if constexpr (KIND == KIND_WGRAD2) {   // dY rows of the gathered tokens
           const uint32_t t = s_tok[rr & (TOKTAB - 1)];
-          off = (klo + rr < khi) ? t * 2 + oa[i] : OOB;
+          return (klo + rr < khi) ? t * 2 + oa[i] : OOB;
         } else {                               // dG13 rows
-          off = (klo + rr < khi) ? (uint32_t)(klo + rr) * (2 * I * 2) + oa[i] : OOB;
+          return (klo + rr < khi) ? (uint32_t)(klo + rr) * (2 * I * 2) + oa[i] : OOB;
         }
       }
-      dma16(ra_src, off, __builtin_amdgcn_readfirstlane(sbase + (i * NW + w_uni) * 1024));
-    }
-#pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      uint32_t off;
+    } else {
+      const int i = q - DA;
       if constexpr (!K_::b_ko) {
-        off = live ? ob[i] + (uint32_t)kt * (BK * 2) : OOB;
+        return live ? ob[i] + (uint32_t)kt * (BK * 2) : OOB;
       } else if constexpr (K_::ragged_rows) {  // weights, dense K rows
-        off = live ? (uint32_t)(kt * BK + kb[i]) * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + ob[i] : OOB;
+        return live ? (uint32_t)(kt * BK + kb[i]) * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + ob[i] : OOB;
       } else {
         const int rr = kt * BK + kb[i];
         if constexpr (KIND == KIND_WGRAD2) {   // Ag rows
-          off = (klo + rr < khi) ? (uint32_t)(klo + rr) * (I * 2) + ob[i] : OOB;
+          return (klo + rr < khi) ? (uint32_t)(klo + rr) * (I * 2) + ob[i] : OOB;
         } else {                               // x rows of the gathered tokens
           const uint32_t t = s_tok[rr & (TOKTAB - 1)];
-          off = (klo + rr < khi) ? t * 2 + ob[i] : OOB;
+          return (klo + rr < khi) ? t * 2 + ob[i] : OOB;
         }
       }
-      dma16(rb_src, off, __builtin_amdgcn_readfirstlane(sbase + BM * BK * 2 + (i * NW + w_uni) * 1024));
     }
+  };
+  // byte offset in a stage of the 1 KiB block that instruction q of this wave fills
+  auto blk_off = [&](int q) __attribute__((always_inline)) -> uint32_t {
+    return q < DA ? (uint32_t)((q * NW + w_uni) * 1024) : (uint32_t)(BM * BK * 2 + ((q - DA) * NW + w_uni) * 1024);
+  };
+  // DMA instruction q (< DA + DB) of K tile kt into stage st (tiles past the
+  // end read zeros)
+  auto issue_one = [&](int kt, int st, int q) __attribute__((always_inline)) {
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
+    dma16(q < DA ? ra_src : rb_src, src_off(kt, q), __builtin_amdgcn_readfirstlane(sbase + blk_off(q)));
+  };
+  auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < DA + DB; ++q) issue_one(kt, st, q);
   };
 
   // LDS row of the j-th 16-row MFMA block of this wave's B sub-tile
@@ -307,8 +319,9 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 
   // All MFMA operands of one K tile are read into registers first, so the
   // tile's LDS stage can be refilled while the MFMAs run.
-  bf16x8_t af[BK / 32][FM], bfr[BK / 32][FN];
-  auto load_frags = [&](int st) __attribute__((always_inline)) {
+  typedef bf16x8_t AFrag[BK / 32][FM];
+  typedef bf16x8_t BFrag[BK / 32][FN];
+  auto load_frags = [&](int st, AFrag& af, BFrag& bfr) __attribute__((always_inline)) {
     const bf16_t* As = smem + st * STAGE;
     const bf16_t* Bs = As + BM * BK;
 #pragma unroll
@@ -325,45 +338,64 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
       }
     }
   };
-  auto mfmas = [&]() __attribute__((always_inline)) {
+  // The MFMAs of one tile with the DMA of tile kt into stage st spread
+  // between them (one DMA instruction every NM / ND MFMAs), so that the
+  // address queue drains while the matrix cores work.
+  auto mfmas_dma = [&](const AFrag& af, const BFrag& bfr, int kt, int st) __attribute__((always_inline)) {
+    constexpr int NM = (BK / 32) * FM * FN, ND = DA + DB;
+    constexpr int SP = NM / ND > 0 ? NM / ND : 1;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          const int idx = (ks * FM + i) * FN + j;
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
-  };
-
-  // ---------------- main loop ----------------
-  // S tiles in flight.  Iteration kt: wait for this wave's DMA of tile kt; a
-  // barrier publishes it; every wave reads its operands into registers; a
-  // second barrier frees the stage, which receives tile kt + S while the
-  // MFMAs run from registers.
-  if constexpr (gathered_k) {
-    if (nk > 0) { fill_tok(0); __syncthreads(); }
-  }
+          if (idx % SP == SP - 1 && idx / SP < ND) {
+            issue_one(kt, st, idx / SP);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
 #pragma unroll
-  for (int st = 0; st < S; ++st) issue_tile(st, st);
-  int st_c = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    vm_wait<(S - 1) * (DA + DB)>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    load_frags(st_c);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    for (int q = NM / SP; q < ND; ++q) issue_one(kt, st, q);   // when there are more DMAs than MFMAs
+  };
+  // the token table of the gathered rows moves on when tile kl starts a new chunk
+  auto refill_tok = [&](int kl) __attribute__((always_inline)) {
     if constexpr (gathered_k) {
-      const int kl = kt + S;
-      if ((kl * BK) % TOKTAB == 0 && kl < nk) {   // rows of tile kl start a new table chunk
+      if ((kl * BK) % TOKTAB == 0 && kl < nk) {
         fill_tok(kl * BK);
         __syncthreads();
       }
     }
-    issue_tile(kt + S, st_c);
-    mfmas();
-    st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+  };
+
+  // ---------------- main loop ----------------
+  if constexpr (gathered_k) {
+    if (nk > 0) { fill_tok(0); __syncthreads(); }
+  }
+  {
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue_tile(st, st);
+    // S tiles in flight.  Iteration kt: wait for this wave's DMA of tile kt; a
+    // barrier publishes it; every wave reads its operands into registers; a
+    // second barrier frees the stage, which receives tile kt + S while the
+    // MFMAs run from registers.
+    AFrag af;
+    BFrag bfr;
+    int st_c = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<(S - 1) * (DA + DB)>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      load_frags(st_c, af, bfr);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      refill_tok(kt + S);
+      mfmas_dma(af, bfr, kt + S, st_c);
+      st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+    }
   }
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
@@ -371,12 +403,12 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim);
 }
 
-// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).
+// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile).
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
 #endif
 #ifndef MOE_CFG_WGRAD
-#define MOE_CFG_WGRAD 128, 128, 2, 2, 2, 4, 32
+#define MOE_CFG_WGRAD 256, 256, 2, 4, 2, 2, 32
 #endif
 using CfgRow = TileCfg<MOE_CFG_ROW>;
 using CfgW = TileCfg<MOE_CFG_WGRAD>;

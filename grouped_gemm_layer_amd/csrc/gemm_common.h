@@ -79,8 +79,20 @@ struct TileCfg {
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
 };
 
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2_t pack4(float a, float b, float c, float d) {
+  return u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// Stores of GEMM outputs.  NT = non-temporal: used for the weight
+// gradients, whose LDS-staged stores write whole lines that this launch
+// never reads again (measured faster); the row kinds' 8- and 16-byte stores
+// need the L2 to combine them into lines (non-temporal is slower there).
+template <bool NT = false, class V, class P>
+__device__ __forceinline__ void st_out(P* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  else *reinterpret_cast<V*>(p) = v;
 }
 
 // Epilogue of one output tile.  acc[i][j][v] holds C[m][n] for
@@ -113,15 +125,16 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         for (int v = 0; v < 4; ++v) av[v] = g1[v] * sigmoid_f32(g1[v]) * g3[v];
         if (a.g13_f32) {   // saved state kept in fp32 (MXFP8 backward quantises from it)
           float* G13 = static_cast<float*>(a.G13);
-          *reinterpret_cast<f32x4_t*>(G13 + (size_t)m * 2 * I + c) = g1;
-          *reinterpret_cast<f32x4_t*>(G13 + (size_t)m * 2 * I + I + c) = g3;
+          st_out(G13 + (size_t)m * 2 * I + c, g1);
+          st_out(G13 + (size_t)m * 2 * I + I + c, g3);
         } else {
           bf16_t* G13 = static_cast<bf16_t*>(a.G13);
-          *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + c) = pack4(g1[0], g1[1], g1[2], g1[3]);
-          *reinterpret_cast<uint2*>(G13 + (size_t)m * 2 * I + I + c) = pack4(g3[0], g3[1], g3[2], g3[3]);
+          st_out(G13 + (size_t)m * 2 * I + c, pack4(g1[0], g1[1], g1[2], g1[3]));
+          st_out(G13 + (size_t)m * 2 * I + I + c, pack4(g3[0], g3[1], g3[2], g3[3]));
         }
-        *reinterpret_cast<uint2*>(Aout + (size_t)m * I + c) = pack4(av[0], av[1], av[2], av[3]);
+        st_out(Aout + (size_t)m * I + c, pack4(av[0], av[1], av[2], av[3]));
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
     }
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
     bf16_t* out = static_cast<bf16_t*>(KIND == KIND_FWD2 ? a.O : a.dXp);
@@ -134,7 +147,7 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         const int n = n0 + wn * WN + 16 * j + ncol;
         if (n >= nlim) continue;
         const f32x4_t v = acc[i][j];
-        *reinterpret_cast<uint2*>(out + (size_t)m * H + n) = pack4(v[0], v[1], v[2], v[3]);
+        st_out(out + (size_t)m * H + n, pack4(v[0], v[1], v[2], v[3]));
       }
     }
   } else if constexpr (KIND == KIND_DGRAD2) {
@@ -184,16 +197,17 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         }
         if constexpr (F32IO) {
           float* dG = static_cast<float*>(a.dG13);
-          *reinterpret_cast<f32x4_t*>(dG + o1) = f32x4_t{d1[0], d1[1], d1[2], d1[3]};
-          *reinterpret_cast<f32x4_t*>(dG + o3) = f32x4_t{d3[0], d3[1], d3[2], d3[3]};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.Ag) + (size_t)m * I + n) = f32x4_t{ag[0], ag[1], ag[2], ag[3]};
+          st_out(dG + o1, f32x4_t{d1[0], d1[1], d1[2], d1[3]});
+          st_out(dG + o3, f32x4_t{d3[0], d3[1], d3[2], d3[3]});
+          st_out(static_cast<float*>(a.Ag) + (size_t)m * I + n, f32x4_t{ag[0], ag[1], ag[2], ag[3]});
         } else {
           bf16_t* dG = static_cast<bf16_t*>(a.dG13);
-          *reinterpret_cast<uint2*>(dG + o1) = pack4(d1[0], d1[1], d1[2], d1[3]);
-          *reinterpret_cast<uint2*>(dG + o3) = pack4(d3[0], d3[1], d3[2], d3[3]);
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.Ag) + (size_t)m * I + n) = pack4(ag[0], ag[1], ag[2], ag[3]);
+          st_out(dG + o1, pack4(d1[0], d1[1], d1[2], d1[3]));
+          st_out(dG + o3, pack4(d3[0], d3[1], d3[2], d3[3]));
+          st_out(static_cast<bf16_t*>(a.Ag) + (size_t)m * I + n, pack4(ag[0], ag[1], ag[2], ag[3]));
         }
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
     }
     // lanes sharing a row, then the WGN waves of a row block, in a fixed order
 #pragma unroll
@@ -216,27 +230,36 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       }
     }
   } else {   // wgrad: fp32 output of one expert, staged through LDS so each
-             // store instruction writes whole rows (full cache lines)
-    static_assert(BM * BN * 4 <= C::SMEM_BYTES, "fp32 tile must fit in the operand LDS");
+             // store instruction writes whole rows (full cache lines); the
+             // tile goes through in chunks of CH rows when it exceeds the LDS
+    constexpr int CH0 = C::SMEM_BYTES / (BN * 4);
+    constexpr int CH = CH0 >= BM ? BM : CH0 >= 128 ? 128 : CH0 >= 64 ? 64 : CH0 >= 32 ? 32 : 16;
+    static_assert(CH * BN * 4 <= C::SMEM_BYTES && BM % CH == 0 && CH % 16 == 0, "fp32 row chunk must fit in the operand LDS");
     float* s_out = reinterpret_cast<float*>(smem);
     constexpr int NQ = BN / 4;                             // 16-byte chunks per row
     auto out_off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ)) << 2); };
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wm * WM + 16 * i + mrow;
-        const int q = (wn * WN + 16 * j + ncol) >> 2;
-        *reinterpret_cast<f32x4_t*>(&s_out[out_off(row, q)]) = acc[i][j];
-      }
-    __syncthreads();
     float* out = (KIND == KIND_WGRAD2) ? a.dw2 + (size_t)e * H * I : a.dw13 + (size_t)e * 2 * I * H;
     const int ld = (KIND == KIND_WGRAD2) ? I : H;
-    for (int c = tid; c < BM * NQ; c += NTHR) {
-      const int row = c / NQ, q = c % NQ;
-      const int m = m0 + row, n = n0 + 4 * q;
-      if (m < mlim && n < nlim)
-        *reinterpret_cast<f32x4_t*>(out + (size_t)m * ld + n) = *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]);
+#pragma unroll
+    for (int ch = 0; ch < BM / CH; ++ch) {
+      if (ch > 0) __syncthreads();                         // the previous chunk has been read out
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * WM + 16 * i + mrow;           // the 16-row block lies in one chunk
+        if ((wm * WM + 16 * i) / CH != ch) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int q = (wn * WN + 16 * j + ncol) >> 2;
+          *reinterpret_cast<f32x4_t*>(&s_out[out_off(row - ch * CH, q)]) = acc[i][j];
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < CH * NQ; c += NTHR) {
+        const int row = c / NQ, q = c % NQ;
+        const int m = m0 + ch * CH + row, n = n0 + 4 * q;
+        if (m < mlim && n < nlim)
+          st_out<true>(out + (size_t)m * ld + n, *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
+      }
     }
   }
 }
