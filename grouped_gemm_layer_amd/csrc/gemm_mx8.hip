@@ -252,7 +252,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
 #define MOE_MX8_CFG_ROW 128, 128, 2, 2, 2, 2, 64
 #endif
 #ifndef MOE_MX8_CFG_WGRAD
-#define MOE_MX8_CFG_WGRAD 128, 128, 2, 2, 2, 2, 64
+#define MOE_MX8_CFG_WGRAD 256, 256, 2, 4, 2, 2, 64
 #endif
 using CfgRow = TileCfg<MOE_MX8_CFG_ROW>;
 using CfgW = TileCfg<MOE_MX8_CFG_WGRAD>;
