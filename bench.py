@@ -258,6 +258,8 @@ def main():
                    "k": d.k, "mode": d.run_mode, "seed": seed},
         "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "route_ms": round(float(np.mean(route_ms)), 4),
+        # the pages' "full layer" timing recomputes the forward (activation checkpointing)
+        "ms_2f_plus_b": round(2.0 * float(np.mean(fwd_ms)) + float(np.mean(bwd_ms)) + float(np.mean(route_ms)), 4),
         "fwd_tflops": round(6.0 * d.M * d.H * d.I / (np.mean(fwd_ms) * 1e-3) / 1e12, 1),
         "bwd_tflops": round(12.0 * d.M * d.H * d.I / (np.mean(bwd_ms) * 1e-3) / 1e12, 1),
         "gemm_tflops": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
