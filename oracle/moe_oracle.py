@@ -38,13 +38,18 @@ The pages print no formula.  The readings taken where they are silent:
   R5  the gate multiplies the expert output in the combine;
   R6  gradient for the routing weights: dgate[t, j] = <dY[t], O_row>; the
       logit gradient is the softmax Jacobian of R1 applied to dgate;
-  R7  MXFP8 (fp8_bwd backward): E4M3FN elements, one E8M0 scale per 32
+  R7  MXFP8 (fp8_bwd backward, mxfp8 mode): E4M3FN elements, one E8M0 scale per 32
       consecutive elements along the GEMM's K; scale exponent X = the smallest
       integer with amax <= 448 * 2**X (clamped to [-127, 127]); element =
       round-to-nearest-even of v / 2**X, saturating at 448; blocks along the
       token dimension start at each expert's first row and the segment tail is
       zero-padded (TE dropless-MoE page, "03 Specialised optimisations":
       group-aware MXFP8 quantisation and MXFP8 grouped GEMM).
+  R12 mxfp8 mode (Prime Mega MoE news page, "How does the fused kernel
+      work?": BF16 and MXFP8 precisions): the forward GEMMs take MXFP8
+      operands quantised along their K (x and W13 along H, A and W2 along I);
+      SwiGLU and the combine stay in full precision; the backward is the
+      fp8_bwd backward applied to this forward's state.
 
 Every function below is pinned by tests/test_oracle_*.py against something
 other than itself (finite differences, closed forms, brute force, the
@@ -59,7 +64,8 @@ __all__ = [
     "Routing", "route", "silu", "sigmoid", "expert_forward", "expert_backward",
     "forward", "backward", "router_backward", "forward_with_gates",
     "e4m3fn_decode_table", "e4m3fn_encode", "mx_scale_exponent", "mx_quant_dequant",
-    "mx_quant_dequant_tokens", "expert_backward_mxfp8", "backward_mxfp8",
+    "mx_quant_dequant_tokens", "expert_backward_mxfp8", "backward_mxfp8", "expert_forward_mxfp8",
+    "forward_mxfp8",
 ]
 
 
@@ -181,6 +187,10 @@ def forward(x, w13, w2, r: Routing):
 
     Returns (Y [T,H] float64, state) where state keeps what the backward needs.
     """
+    return _layer_forward(x, w13, w2, r, expert_forward)
+
+
+def _layer_forward(x, w13, w2, r: Routing, expert_fn):
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
     k = r.k
@@ -194,7 +204,7 @@ def forward(x, w13, w2, r: Routing):
     for e, a, b in _segments(r):
         if b == a:
             continue
-        f = expert_forward(x[tok[a:b]], w13[e], w2[e])
+        f = expert_fn(x[tok[a:b]], w13[e], w2[e])
         O[a:b], G1[a:b], G3[a:b], A[a:b] = f["O"], f["G1"], f["G3"], f["A"]
     # combine: gather each token's k rows back in slot order, weight by its gates
     Orows = O[r.flat_to_sorted].reshape(T, k, H)
@@ -401,3 +411,25 @@ def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
     dgate = dgate_sorted[r.flat_to_sorted].reshape(T, k)
     dlogits = router_backward(r.gate, dgate, r.idx, E)
     return {"dx": dX, "dw13": dW13, "dw2": dW2, "dgate": dgate, "dlogits": dlogits}
+
+
+def expert_forward_mxfp8(xrows, w13e, w2e) -> dict:
+    """One expert's forward in the mxfp8 mode (R12): both GEMMs take MXFP8
+    operands, each quantised along that GEMM's K:
+      G13 = Q_H(X) Q_H(W13[e])^T,  A = SiLU(G1) * G3,  O = Q_I(A) Q_I(W2[e])^T
+    (W13[e] is [2I, H] and W2[e] is [H, I]: K is their last axis)."""
+    X = np.asarray(xrows, dtype=np.float64)
+    W13 = np.asarray(w13e, dtype=np.float64)
+    W2 = np.asarray(w2e, dtype=np.float64)
+    I = W13.shape[0] // 2
+    G = mx_quant_dequant(X, axis=1)[0] @ mx_quant_dequant(W13, axis=1)[0].T
+    G1, G3 = G[:, :I], G[:, I:]
+    A = silu(G1) * G3
+    O = mx_quant_dequant(A, axis=1)[0] @ mx_quant_dequant(W2, axis=1)[0].T
+    return {"G1": G1, "G3": G3, "A": A, "O": O}
+
+
+def forward_mxfp8(x, w13, w2, r: Routing):
+    """Layer forward of the mxfp8 mode: forward() with expert_forward_mxfp8.
+    Its backward is backward_mxfp8 applied to the state returned here."""
+    return _layer_forward(x, w13, w2, r, expert_forward_mxfp8)

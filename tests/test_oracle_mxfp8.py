@@ -156,3 +156,64 @@ def test_quantised_operands_are_blocked_along_each_gemms_k(monkeypatch):
     expected = [dYp, g[:, None] * fwd["A"], out["dG"], Xp]
     for ref in expected:
         assert any(a.shape == ref.shape and np.array_equal(a, ref) for a in arrays)
+
+
+def test_mxfp8_forward_with_identity_quantiser_is_exact(monkeypatch):
+    d = mi.LayerDims(T=96, H=64, I=32, E=5, k=2, dtype="fp32")
+    inp = mi.make_inputs(d, 8)
+    r = orc.route(inp["logits"], d.k)
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    monkeypatch.setattr(orc, "mx_quant_dequant", lambda a, axis=-1: (np.asarray(a, np.float64), None, None))
+    Yq, stq = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r)
+    assert np.max(np.abs(Yq - Y)) <= 1e-12 * np.max(np.abs(Y))
+    for key in ("G1", "G3", "A", "O"):
+        assert np.max(np.abs(stq[key] - st[key])) <= 1e-12 * np.max(np.abs(st[key]))
+
+
+def test_mxfp8_forward_operands_blocked_along_k(monkeypatch):
+    rng = np.random.default_rng(9)
+    n, H, I = 24, 64, 32
+    calls = []
+
+    def rec(a, axis=-1):
+        a = np.asarray(a, np.float64)
+        calls.append((a.shape, axis % a.ndim))
+        return a, None, None
+
+    monkeypatch.setattr(orc, "mx_quant_dequant", rec)
+    orc.expert_forward_mxfp8(rng.standard_normal((n, H)), rng.standard_normal((2 * I, H)),
+                             rng.standard_normal((H, I)))
+    # x [n, H] and W13 [2I, H] along H; A [n, I] and W2 [H, I] along I
+    assert sorted(calls) == sorted([((n, H), 1), ((2 * I, H), 1), ((n, I), 1), ((H, I), 1)])
+
+
+def test_mxfp8_forward_exact_on_representable_operands():
+    """x and W13 built from E4M3 codes times one power of two per 32-block are
+    MXFP8 values already: the first GEMM (G1, G3) must equal the exact one."""
+    rng = np.random.default_rng(10)
+    tab = orc.e4m3fn_decode_table()
+    finite = np.array([c for c in range(256) if not np.isnan(tab[c])])
+
+    def representable(rows, cols):
+        codes = rng.choice(finite, size=(rows, cols))
+        v = tab[codes]
+        v[:, ::32] = 448.0 * np.sign(v[:, ::32] + 0.5)        # every block holds amax 448 * 2^X
+        scale = np.exp2(rng.integers(-6, 4, size=(rows, cols // 32))).repeat(32, axis=1)
+        return v * scale
+
+    x, w13 = representable(40, 64), representable(2 * 32, 64)
+    w2 = rng.standard_normal((64, 32))
+    q = orc.expert_forward_mxfp8(x, w13, w2)
+    e = orc.expert_forward(x, w13, w2)
+    assert np.array_equal(q["G1"], e["G1"]) and np.array_equal(q["G3"], e["G3"])
+    assert not np.array_equal(q["O"], e["O"])                  # A is not representable
+
+
+def test_mxfp8_forward_close_to_exact():
+    d = mi.LayerDims(T=128, H=128, I=64, E=4, k=2, dtype="bf16", mode="mxfp8")
+    inp = mi.make_inputs(d, 11)
+    r = orc.route(inp["logits"], d.k)
+    Y, _ = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    Yq, _ = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r)
+    rel = np.max(np.abs(Yq - Y)) / np.max(np.abs(Y))
+    assert 1e-4 < rel < 0.15, rel
