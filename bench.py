@@ -31,6 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 operands)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
+FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_a", "quant_w2", "gemm2", "combine"]
 BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
 BWD_KERNELS_FP8 = ["tile_table_b", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t", "quant_dg",
                    "dgrad1", "unpermute_reduce", "router_bwd", "pad_offsets", "quant_dyt", "quant_agt", "wgrad2",
@@ -71,11 +72,13 @@ def hbm_bytes(d):
     codes + one scale byte per 32 codes)."""
     rows = d.M * d.H * 2 + d.T * d.H * 2
     q = lambda n: n * 2 + n + n // 32            # read bf16, write codes + scales
+    q4 = lambda n: n * 4 + n + n // 32           # read fp32, write codes + scales
     H, I, E, M, T = d.H, d.I, d.E, d.M, d.T
     return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4,
             "quant_w2t": q(E * H * I), "quant_w13t": q(E * 2 * I * H), "quant_dy": q(T * H),
             "quant_dg": q(M * 2 * I), "quant_dyt": q(M * H), "quant_agt": q(M * I), "quant_dgt": q(M * 2 * I),
-            "quant_xt": q(M * H)}
+            "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H), "quant_a": q4(M * I),
+            "quant_w2": q(E * H * I)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -155,6 +158,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--mode", choices=["bf16", "mxfp8", "fp8_bwd"], default=None,
+                    help="run the configuration's shape in another precision mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the timed region (counter calibration)")
     args = ap.parse_args()
@@ -169,8 +174,13 @@ def main():
     import grouped_gemm_layer_amd as g
 
     d = mi.CONFIGS[args.config]
+    workload = mi.CONFIG_NAMES[args.config]
+    if args.mode is not None and args.mode != d.run_mode:
+        import dataclasses
+        d = dataclasses.replace(d, mode=args.mode)
+        workload += f", {args.mode} mode"
     seed = args.config if args.seed is None else args.seed
-    print(f"[bench] config {args.config}: {mi.CONFIG_NAMES[args.config]}", file=sys.stderr, flush=True)
+    print(f"[bench] config {args.config}: {workload}", file=sys.stderr, flush=True)
     inp = mi.make_inputs(d, seed)
     torch.cuda.set_device(0)
     layer = g.MoeLayer(d.T, d.H, d.I, d.E, d.k, mode=d.run_mode)
@@ -184,11 +194,14 @@ def main():
 
     ev = HipEvents()
     nf, nb = g.num_kernels(layer.dims, "forward"), g.num_kernels(layer.dims, "backward")
-    fp8_bwd = d.run_mode == "fp8_bwd"
+    fp8_bwd = d.run_mode in ("fp8_bwd", "mxfp8")
+    fp8_fwd = d.run_mode == "mxfp8"
+    fwd_names = FWD_KERNELS_MX8 if fp8_fwd else FWD_KERNELS
     bwd_names = BWD_KERNELS_FP8 if fp8_bwd else BWD_KERNELS
-    assert nf == len(FWD_KERNELS) and nb == len(bwd_names)
-    peak = {n: (PEAK_FP8_TFLOPS if fp8_bwd and n in ("dgrad2_dswiglu", "dgrad1", "wgrad2", "wgrad1")
-                else PEAK_BF16_TFLOPS) for n in FWD_KERNELS + bwd_names}
+    assert nf == len(fwd_names) and nb == len(bwd_names)
+    fp8_gemms = (("gemm1_swiglu", "gemm2") if fp8_fwd else ()) + \
+        (("dgrad2_dswiglu", "dgrad1", "wgrad2", "wgrad1") if fp8_bwd else ())
+    peak = {n: (PEAK_FP8_TFLOPS if n in fp8_gemms else PEAK_BF16_TFLOPS) for n in fwd_names + bwd_names}
     K, W = args.steps, args.warmup
     fev = [ev.create(nf + 1) for _ in range(K)]
     bev = [ev.create(nb + 1) for _ in range(K)]
@@ -217,12 +230,12 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    names = FWD_KERNELS + bwd_names
+    names = fwd_names + bwd_names
     per = {n: [] for n in names}
     fwd_ms, bwd_ms, route_ms = [], [], []
     for i in range(K):
         for j in range(nf):
-            per[FWD_KERNELS[j]].append(ev.elapsed(fev[i][j], fev[i][j + 1]))
+            per[fwd_names[j]].append(ev.elapsed(fev[i][j], fev[i][j + 1]))
         for j in range(nb):
             per[bwd_names[j]].append(ev.elapsed(bev[i][j], bev[i][j + 1]))
         fwd_ms.append(ev.elapsed(fev[i][0], fev[i][nf]))
@@ -253,8 +266,9 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8_bwd": "bf16 fwd + mxfp8 bwd"}[d.run_mode], "data": "synthetic",
-        "config": {"workload": mi.CONFIG_NAMES[args.config], "T": d.T, "H": d.H, "I": d.I, "E": d.E,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8_bwd": "bf16 fwd + mxfp8 bwd", "mxfp8": "mxfp8"}[d.run_mode],
+        "data": "synthetic",
+        "config": {"workload": workload, "T": d.T, "H": d.H, "I": d.I, "E": d.E,
                    "k": d.k, "mode": d.run_mode, "seed": seed},
         "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "route_ms": round(float(np.mean(route_ms)), 4),

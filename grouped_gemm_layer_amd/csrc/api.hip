@@ -23,6 +23,7 @@ struct Sizes {
   // carving offsets
   size_t r_partials, r_bases;
   size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
+  size_t f_qx, f_sx, f_qw13, f_sw13, f_qa, f_sa, f_qw2, f_sw2;   // mxfp8 forward operands
   size_t b_tile_e, b_tile_r, b_tile_x, b_dG13, b_Ag, b_dXp, b_part;
   // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
   size_t Mp;
@@ -35,10 +36,12 @@ moe_status check_dims(const moe_dims* d) {
   if (d->T <= 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k <= 0 || d->k > d->E) return MOE_ERR_DIMS;
   if ((int64_t)d->T * d->k > INT32_MAX) return MOE_ERR_DIMS;
   if ((int64_t)d->E * 2 * d->I * d->H > ((int64_t)1 << 40)) return MOE_ERR_DIMS;
-  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_FP8_BWD)
+  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_MXFP8 &&
+      d->mode != MOE_MODE_FP8_BWD)
     return MOE_ERR_UNSUPPORTED;
   if (d->H % 64 != 0 || d->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (d->mode == MOE_MODE_FP8_BWD && d->H % MX_KTILE != 0) return MOE_ERR_UNSUPPORTED;
+  if (mx8_backward(d->mode) && d->H % MX_KTILE != 0) return MOE_ERR_UNSUPPORTED;
+  if (mx8_forward(d->mode) && d->I % MX_KTILE != 0) return MOE_ERR_UNSUPPORTED;
   if (d->E > 512 || d->k > 32) return MOE_ERR_UNSUPPORTED;
   // every per-operand buffer is addressed with 32-bit byte offsets
   const int64_t M = (int64_t)d->T * d->k;
@@ -46,7 +49,7 @@ moe_status check_dims(const moe_dims* d) {
   const int64_t es = d->mode == MOE_MODE_FP32 ? 4 : 2;
   if (M * wide * es >= ((int64_t)1 << 31) || (int64_t)2 * d->I * d->H * es >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
-  if (d->mode == MOE_MODE_FP8_BWD && (int64_t)mx_token_capacity((size_t)M, d->E) * wide >= ((int64_t)1 << 31))
+  if (mx8_backward(d->mode) && (int64_t)mx_token_capacity((size_t)M, d->E) * wide >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -63,14 +66,22 @@ Sizes compute_sizes(const moe_dims* d) {
   s.r_bases = o;    o += align_up(nblk * d->E * 4);
   s.route_ws = o;
   // fp8_bwd keeps the quantisers' inputs (G13, dG13, gate*A) in fp32
-  const size_t es_q = (d->mode == MOE_MODE_FP8_BWD) ? 4 : es;
+  const size_t es_q = mx8_backward(d->mode) ? 4 : es;
   s.saved = align_up(M * 2 * d->I * es_q);
   o = 0;
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
   s.f_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
-  s.f_A = o;      o += align_up(M * d->I * es);
+  s.f_A = o;      o += align_up(M * d->I * (mx8_forward(d->mode) ? 4 : es));   // fp32 when it is quantised
   s.f_O = o;      o += align_up(M * d->H * es);
+  if (mx8_forward(d->mode)) {
+    const size_t T = d->T, H = d->H, I = d->I, E = d->E;
+    auto take = [&](size_t& at_, size_t bytes) { at_ = o; o += align_up(bytes); };
+    take(s.f_qx, T * H);          take(s.f_sx, T * H / 32);
+    take(s.f_qw13, E * 2 * I * H); take(s.f_sw13, E * 2 * I * H / 32);
+    take(s.f_qa, M * I);          take(s.f_sa, M * I / 32);
+    take(s.f_qw2, E * H * I);     take(s.f_sw2, E * H * I / 32);
+  }
   s.fwd_ws = o;
   o = 0;
   s.b_tile_e = o; o += align_up(max_tiles_b * 4);
@@ -80,7 +91,7 @@ Sizes compute_sizes(const moe_dims* d) {
   s.b_Ag = o;     o += align_up(M * d->I * es_q);
   s.b_dXp = o;    o += align_up(M * d->H * es);
   s.b_part = o;   o += align_up((size_t)dgrad2_parts(d->mode, d->I) * M * 4);
-  if (d->mode == MOE_MODE_FP8_BWD) {
+  if (mx8_backward(d->mode)) {
     const size_t T = d->T, H = d->H, I = d->I, E = d->E;
     const size_t Mp = mx_token_capacity(M, d->E);
     s.Mp = Mp;
@@ -156,12 +167,15 @@ struct Marks {
 // kernels per call, in launch order
 constexpr int kRouteKernels = 4;      // topk+gate, histogram, scan, scatter
 constexpr int kForwardKernels = 4;    // tile table, GEMM1+SwiGLU, GEMM2, combine
+// mxfp8: tile table, quant x, quant W13, GEMM1+SwiGLU, quant A, quant W2, GEMM2, combine
+constexpr int kForwardKernelsMx8 = 8;
+inline int forward_kernels(int mode) { return mx8_forward(mode) ? kForwardKernelsMx8 : kForwardKernels; }
 constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13
 // fp8_bwd: tile table, quant W2^T, quant dY, dgrad W2, quant W13^T, quant dG13,
 // dgrad W13, unpermute, router, padded offsets, quant dY^T, quant (gA)^T,
 // wgrad W2, quant dG13^T, quant x^T, wgrad W13
 constexpr int kBackwardKernelsMx8 = 16;
-inline int backward_kernels(int mode) { return mode == MOE_MODE_FP8_BWD ? kBackwardKernelsMx8 : kBackwardKernels; }
+inline int backward_kernels(int mode) { return mx8_backward(mode) ? kBackwardKernelsMx8 : kBackwardKernels; }
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
@@ -221,7 +235,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   LayerArgs a = base_args(dims, routing);
   a.x = x; a.w13 = w13; a.w2 = w2;
   a.G13 = saved;
-  a.g13_f32 = dims->mode == MOE_MODE_FP8_BWD;
+  a.g13_f32 = mx8_backward(dims->mode);
   a.A = at(ws, s.f_A);
   a.O = at(ws, s.f_O);
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.f_tile_e));
@@ -230,12 +244,35 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
   const int bm = fwd_row_tile_m(dims->mode);
   hipError_t e = mk.mark();
-  if (e == hipSuccess) e = launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_FWD1, a, stream);
-  if (e == hipSuccess) e = mk.mark();
-  if (e == hipSuccess) e = gemm(bf16, KIND_FWD2, a, stream);
-  if (e == hipSuccess) e = mk.mark();
+  auto step = [&](hipError_t r) {   // record kernel completion, keep the first error
+    if (e == hipSuccess) e = r;
+    if (e == hipSuccess) e = mk.mark();
+  };
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream));
+  if (mx8_forward(dims->mode)) {
+    auto u8 = [&](size_t off) { return reinterpret_cast<uint8_t*>(at(ws, off)); };
+    Mx8Args q{};
+    q.qx = u8(s.f_qx);     q.sx = u8(s.f_sx);
+    q.qw13 = u8(s.f_qw13); q.sw13 = u8(s.f_sw13);
+    q.qa = u8(s.f_qa);     q.sa = u8(s.f_sa);
+    q.qw2 = u8(s.f_qw2);   q.sw2 = u8(s.f_sw2);
+    const bf16_t* x16 = static_cast<const bf16_t*>(x);
+    if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_rows(static_cast<const bf16_t*>(w13), a.E * 2 * a.I, a.H, nullptr, 1, u8(s.f_qw13),
+                                u8(s.f_sw13), stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_rows(static_cast<const float*>(a.A), a.M, a.I, nullptr, 1, u8(s.f_qa), u8(s.f_sa),
+                                stream));
+    if (e == hipSuccess)
+      step(launch_mx_quant_rows(static_cast<const bf16_t*>(w2), a.E * a.H, a.I, nullptr, 1, u8(s.f_qw2),
+                                u8(s.f_sw2), stream));
+    if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
+  } else {
+    if (e == hipSuccess) step(gemm(bf16, KIND_FWD1, a, stream));
+    if (e == hipSuccess) step(gemm(bf16, KIND_FWD2, a, stream));
+  }
   if (e == hipSuccess) {
     if (bf16)
       e = launch_combine<bf16_t>(static_cast<const bf16_t*>(a.O), a.f2s, a.gate, a.T, a.k, a.H,
@@ -243,8 +280,8 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     else
       e = launch_combine<float>(static_cast<const float*>(a.O), a.f2s, a.gate, a.T, a.k, a.H,
                                 static_cast<float*>(y), stream);
+    if (e == hipSuccess) e = mk.mark();
   }
-  if (e == hipSuccess) e = mk.mark();
   return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -275,7 +312,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
   const int bm = bwd_row_tile_m(dims->mode);
-  const bool mx8 = dims->mode == MOE_MODE_FP8_BWD;
+  const bool mx8 = mx8_backward(dims->mode);
   const Mx8Args q = mx8 ? mx8_args(s, ws) : Mx8Args{};
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
   const bf16_t* x16 = static_cast<const bf16_t*>(x);
@@ -356,14 +393,14 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
 
 int moe_num_kernels(const moe_dims* dims, int which) {
   if (check_dims(dims) != MOE_OK) return -1;
-  return which == 0 ? kRouteKernels : which == 1 ? kForwardKernels : which == 2 ? backward_kernels(dims->mode) : -1;
+  return which == 0 ? kRouteKernels : which == 1 ? forward_kernels(dims->mode) : which == 2 ? backward_kernels(dims->mode) : -1;
 }
 
 moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                              const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events, int n_events) {
   if (!events) return MOE_ERR_NULL;
-  if (n_events < kForwardKernels + 1) return MOE_ERR_DIMS;
+  if (check_dims(dims) == MOE_OK && n_events < forward_kernels(dims->mode) + 1) return MOE_ERR_DIMS;
   return forward_impl(dims, x, w13, w2, routing, y, saved, ws, ws_bytes, stream,
                       Marks{events, n_events, 0, stream});
 }

@@ -132,7 +132,10 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
           st_out(G13 + (size_t)m * 2 * I + c, pack4(g1[0], g1[1], g1[2], g1[3]));
           st_out(G13 + (size_t)m * 2 * I + I + c, pack4(g3[0], g3[1], g3[2], g3[3]));
         }
-        st_out(Aout + (size_t)m * I + c, pack4(av[0], av[1], av[2], av[3]));
+        if constexpr (F32IO)   // the input of the MXFP8 quantiser of A
+          st_out(reinterpret_cast<float*>(a.A) + (size_t)m * I + c, f32x4_t{av[0], av[1], av[2], av[3]});
+        else
+          st_out(Aout + (size_t)m * I + c, pack4(av[0], av[1], av[2], av[3]));
       }
       __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
     }

@@ -9,9 +9,13 @@
 // dropless-MoE page, "03 Specialised optimisations": group-aware MXFP8
 // quantisation with MXFP8 grouped GEMM).
 //
+// mxfp8 mode (the same page's BF16/MXFP8 precisions): the forward GEMMs too.
+//
 // Every kernel computes C[m][n] = sum_k A[m][k] B[n][k] over one BM x BN
 // tile, both operands stored K-contiguous (codes [rows][K], scales
 // [rows][K/32]):
+//   GEMM W13 + SwiGLU (KIND_FWD1): A = x[tok(r)] (gathered), B = W13[e] rows; K = H
+//   GEMM W2      (KIND_FWD2):  A = A rows,               B = W2[e] rows;  K = I
 //   dgrad of W2   (KIND_DGRAD2): A = dY[tok(r)] (gathered), B = W2[e]^T;  K = H
 //   dgrad of W13  (KIND_DGRAD1): A = dG13 rows,            B = W13[e]^T; K = 2I
 //   wgrad of W2   (KIND_WGRAD2): A = dY^T, B = (gate A)^T;   K = tokens of e
@@ -68,7 +72,7 @@ __device__ __forceinline__ int frag_scale(const uint8_t* stile, int row0, int la
 }
 
 template <int KIND> struct MxKind {
-  static constexpr bool ragged_rows = (KIND == KIND_DGRAD2 || KIND == KIND_DGRAD1);
+  static constexpr bool ragged_rows = (KIND != KIND_WGRAD2 && KIND != KIND_WGRAD1);
 };
 
 template <int KIND, class C>
@@ -101,8 +105,8 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     e = rt.e;
     m0 = rt.m0;
     mlim = rt.mlim;
-    n0 = rt.nt * BN;
-    nk = (KIND == KIND_DGRAD2 ? H : 2 * I) / KT;
+    n0 = rt.nt * (KIND == KIND_FWD1 ? BN / 2 : BN);
+    nk = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 ? H : KIND == KIND_FWD2 ? I : 2 * I) / KT;
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
     e = L / per_e;
@@ -113,13 +117,19 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     nk = (a.offsets[e + 1] - a.offsets[e] + KT - 1) / KT;
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
-  const int nlim = (KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
+  const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
 
   // ---------------- operands ----------------
   // codes / scales buffers, row length in bytes (K) of each operand
   const uint8_t *ca, *sa_, *cb, *sb_;
   int lda, ldb, arows, brows;
-  if constexpr (KIND == KIND_DGRAD2) {
+  if constexpr (KIND == KIND_FWD1) {           // x rows (gathered) x W13[e] rows, K = H
+    ca = q.qx; sa_ = q.sx; lda = H; arows = a.T;
+    cb = q.qw13 + (size_t)e * 2 * I * H; sb_ = q.sw13 + (size_t)e * 2 * I * (H / 32); ldb = H; brows = 2 * I;
+  } else if constexpr (KIND == KIND_FWD2) {    // A rows x W2[e] rows, K = I
+    ca = q.qa; sa_ = q.sa; lda = I; arows = a.M;
+    cb = q.qw2 + (size_t)e * H * I; sb_ = q.sw2 + (size_t)e * H * (I / 32); ldb = I; brows = H;
+  } else if constexpr (KIND == KIND_DGRAD2) {
     ca = q.qdy; sa_ = q.sdy; lda = H; arows = a.T;
     cb = q.qw2t + (size_t)e * I * H; sb_ = q.sw2t + (size_t)e * I * (H / 32); ldb = H; brows = I;
   } else if constexpr (KIND == KIND_DGRAD1) {
@@ -139,10 +149,25 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
 
   // source row (of the operand's buffer) of tile row rl
   auto a_src_row = [&](int rl) -> uint32_t {
-    if constexpr (KIND == KIND_DGRAD2) return (uint32_t)(a.s2f[min(m0 + rl, mlim - 1)] / k);
+    if constexpr (KIND == KIND_DGRAD2 || KIND == KIND_FWD1) return (uint32_t)(a.s2f[min(m0 + rl, mlim - 1)] / k);
     else return (uint32_t)min(m0 + rl, mlim - 1);
   };
-  auto b_src_row = [&](int nl) -> uint32_t { return (uint32_t)min(n0 + nl, nlim - 1); };
+  auto b_src_row = [&](int nl) -> uint32_t {
+    if constexpr (KIND == KIND_FWD1) {         // tile rows [0, BN/2) are W1 rows, the rest the matching W3 rows
+      const int c = min(n0 + (nl & (BN / 2 - 1)), I - 1);
+      return (uint32_t)((nl < BN / 2) ? c : I + c);
+    } else {
+      return (uint32_t)min(n0 + nl, nlim - 1);
+    }
+  };
+  // LDS row of the j-th 16-row MFMA block of this wave's B sub-tile (the
+  // SwiGLU kind pairs each W1 block with its W3 block)
+  auto brow = [&](int j) -> int {
+    if constexpr (KIND == KIND_FWD1)
+      return (j < FN / 2) ? wn * (WN / 2) + 16 * j : BN / 2 + wn * (WN / 2) + 16 * (j - FN / 2);
+    else
+      return wn * WN + 16 * j;
+  };
 
   // DMA instruction i of wave w fills 1 KiB block ci = i*NW + w of a code
   // tile: 8 rows of 128 bytes; lane l writes physical chunk l%8 of row
@@ -211,8 +236,8 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      bfr[j] = frag_codes(base + B_CODES, wn * WN + 16 * j, lane);
-      bs[j] = frag_scale(base + B_SC, wn * WN + 16 * j, lane);
+      bfr[j] = frag_codes(base + B_CODES, brow(j), lane);
+      bs[j] = frag_scale(base + B_SC, brow(j), lane);
     }
   };
   auto mfmas = [&]() __attribute__((always_inline)) {
@@ -261,8 +286,9 @@ template <int KIND, class C>
 hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
   int n_tiles, tiles;
   if constexpr (MxKind<KIND>::ragged_rows) {
-    const int ncols = (KIND == KIND_DGRAD2) ? a.I : a.H;
-    n_tiles = (ncols + C::BN - 1) / C::BN;
+    const int ncols = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) ? a.I : a.H;
+    const int bn = (KIND == KIND_FWD1) ? C::BN / 2 : C::BN;
+    n_tiles = (ncols + bn - 1) / bn;
     tiles = n_tiles * max_row_tiles(a.M, a.E, C::BM);
   } else {
     const int mdim = (KIND == KIND_WGRAD2) ? a.H : 2 * a.I;
@@ -282,6 +308,8 @@ int mx8_dgrad2_tile_n() { return CfgRow::BN; }
 
 hipError_t launch_gemm_mx8(GemmKind kind, const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
   switch (kind) {
+    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRow>(a, q, s);
+    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRow>(a, q, s);
     case KIND_DGRAD2: return launch_kind<KIND_DGRAD2, CfgRow>(a, q, s);
     case KIND_DGRAD1: return launch_kind<KIND_DGRAD1, CfgRow>(a, q, s);
     case KIND_WGRAD2: return launch_kind<KIND_WGRAD2, CfgW>(a, q, s);

@@ -97,6 +97,11 @@ struct Mx8Args {
   const uint8_t *qagt, *sagt;   // [I][Mp]     gate * A, K = tokens
   const uint8_t *qdgt, *sdgt;   // [2I][Mp]    dG13, K = tokens
   const uint8_t *qxt, *sxt;     // [H][Mp]     gathered x, K = tokens
+  // mxfp8 forward
+  const uint8_t *qx, *sx;       // [T][H]      x rows, K = H
+  const uint8_t *qw13, *sw13;   // [E][2I][H]  W13 rows, K = H
+  const uint8_t *qa, *sa;       // [M][I]      A rows, K = I
+  const uint8_t *qw2, *sw2;     // [E][H][I]   W2 rows, K = I
 };
 // Padded token capacity: every expert rounds its count up to MX_KTILE.
 inline size_t mx_token_capacity(size_t M, int E) {
@@ -141,7 +146,7 @@ hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s);
 hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s);
 
-// MXFP8 backward GEMMs (kind = KIND_DGRAD2 .. KIND_WGRAD1)
+// MXFP8 GEMMs (every kind)
 hipError_t launch_gemm_mx8(GemmKind kind, const LayerArgs& a, const Mx8Args& q, hipStream_t s);
 int mx8_row_tile_m();       // token rows per tile of the row-ragged MXFP8 GEMMs
 int mx8_dgrad2_tile_n();    // columns per tile of the MXFP8 dgrad of W2
@@ -169,14 +174,18 @@ int bf16_row_tile_m();      // token rows per tile of the row-ragged bf16 GEMMs
 int bf16_dgrad2_tile_n();   // columns per tile of the bf16 dgrad of W2
 constexpr int FP32_BM = 64;
 constexpr int FP32_BN = 64;
-// mode: 0 fp32, 1 bf16, 3 fp8_bwd (the public moe_mode values)
-inline int fwd_row_tile_m(int mode) { return mode == 0 ? FP32_BM : bf16_row_tile_m(); }
+// mode: 0 fp32, 1 bf16, 2 mxfp8, 3 fp8_bwd (the public moe_mode values)
+inline bool mx8_forward(int mode) { return mode == 2; }
+inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
+inline int fwd_row_tile_m(int mode) {
+  return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
+}
 inline int bwd_row_tile_m(int mode) {
-  return mode == 0 ? FP32_BM : mode == 3 ? mx8_row_tile_m() : bf16_row_tile_m();
+  return mode == 0 ? FP32_BM : mx8_backward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
 }
 inline int dgrad2_parts(int mode, int I) {
   // N tiles of the dgrad of W2 (N = I): one gate-gradient partial per tile
-  const int bn = mode == 0 ? FP32_BN : mode == 3 ? mx8_dgrad2_tile_n() : bf16_dgrad2_tile_n();
+  const int bn = mode == 0 ? FP32_BN : mx8_backward(mode) ? mx8_dgrad2_tile_n() : bf16_dgrad2_tile_n();
   return (I + bn - 1) / bn;
 }
 

@@ -37,8 +37,9 @@
  * Element type of x/dy/y/dx/w13/w2: fp32 in MOE_MODE_FP32, bf16 (raw 16-bit
  * patterns) otherwise.  Gates, gate/logit gradients and weight gradients are
  * always fp32.  Current limits: H and I multiples of 64 (H a multiple of 128
- * in MOE_MODE_FP8_BWD), E <= 512, k <= 32, and every activation-sized buffer
- * below 2 GiB (MOE_ERR_UNSUPPORTED otherwise).
+ * in MOE_MODE_FP8_BWD, H and I multiples of 128 in MOE_MODE_MXFP8), E <= 512,
+ * k <= 32, and every activation-sized buffer below 2 GiB (MOE_ERR_UNSUPPORTED
+ * otherwise).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -54,7 +55,7 @@ extern "C" {
 typedef enum {
   MOE_MODE_FP32 = 0,     /* fp32 activations/weights (debug and tiny shapes) */
   MOE_MODE_BF16 = 1,     /* bf16 storage, fp32 accumulation, MFMA GEMMs */
-  MOE_MODE_MXFP8 = 2,    /* reserved: MXFP8 forward and backward (not built; MOE_ERR_UNSUPPORTED) */
+  MOE_MODE_MXFP8 = 2,    /* MXFP8 forward GEMMs and the fp8_bwd backward (see moe_forward) */
   MOE_MODE_FP8_BWD = 3   /* bf16 forward, MXFP8 backward GEMMs (see moe_backward) */
 } moe_mode;
 
@@ -108,7 +109,13 @@ moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routin
  *   y[t]   = sum_j gate[t,j] * O[flat_to_sorted[t*k+j]]               (fp32 sum in slot order)
  * x, w13, w2: device inputs; y: device output [T,H]; saved: device buffer of
  * the size reported (G13 of every routed row), to be passed unchanged to
- * moe_backward. */
+ * moe_backward.
+ *
+ * MOE_MODE_MXFP8 (Prime Mega MoE news page, "How does the fused kernel
+ * work?": BF16 and MXFP8 precisions): both GEMMs read their operands as
+ * MXFP8 quantised along K as moe_mxfp8_quantize describes (x and W13 along H,
+ * A and W2 along I; A is quantised from its fp32 value); SwiGLU, the combine
+ * and y stay as above.  Its backward is the MOE_MODE_FP8_BWD backward. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                        const moe_routing* routing, void* y, void* saved,
                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -149,9 +156,11 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  * n_events >= moe_num_kernels(...) + 1 events created by the caller
  * (MOE_ERR_NULL / MOE_ERR_DIMS otherwise).  Kernel order:
  *   forward : tile table, GEMM W13 + SwiGLU, GEMM W2, combine
+ *   forward, MOE_MODE_MXFP8: tile table, quantise x, quantise W13, GEMM W13 +
+ *             SwiGLU, quantise A, quantise W2, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
  *             unpermute-reduce, router backward, wgrad W2, wgrad W13
- *   backward, MOE_MODE_FP8_BWD: tile table, quantise W2^T, quantise dy,
+ *   backward, MOE_MODE_FP8_BWD and MOE_MODE_MXFP8: tile table, quantise W2^T, quantise dy,
  *             dgrad W2 + SwiGLU derivative, quantise W13^T, quantise dG13,
  *             dgrad W13, unpermute-reduce, router backward, padded expert
  *             offsets, quantise dy^T, quantise (gate*A)^T, wgrad W2,

@@ -116,16 +116,20 @@ def oracle_expert_wgrad(orc, inp: dict, r, e: int) -> dict:
     return {"dw13": bw["dW13"], "dw2": bw["dW2"]}
 
 
-def oracle_token_rows_mx8(orc, inp: dict, r, tokens) -> dict:
-    """dX, dgate, dlogits of the given tokens under the fp8_bwd backward.
+def oracle_token_rows_mx8(orc, inp: dict, r, tokens, fwd=None) -> dict:
+    """y, dX, dgate, dlogits of the given tokens under the fp8_bwd backward
+    (fwd = the oracle's per-expert forward: expert_forward for fp8_bwd,
+    expert_forward_mxfp8 for the mxfp8 mode).
 
     Row-wise quantisation (along H and 2I) treats each row on its own, so the
     rows of the sampled tokens are evaluated expert by expert with the
     oracle's per-expert fp8_bwd function (its weight gradients, which depend
     on all rows of the expert, are not used here)."""
+    fwd = fwd or orc.expert_forward
     k = r.k
     x, w13, w2, dy = inp["x"], inp["w13"], inp["w2"], inp["dy"]
     H = x.shape[1]
+    Y = np.zeros((len(tokens), H))
     dX = np.zeros((len(tokens), H))
     dgate = np.zeros((len(tokens), k))
     by_e = {}
@@ -135,17 +139,19 @@ def oracle_token_rows_mx8(orc, inp: dict, r, tokens) -> dict:
     for e, rows in by_e.items():
         toks = np.array([t for _, t, _ in rows])
         g = np.array([r.gate[t, j] for _, t, j in rows])
-        f = orc.expert_forward(x[toks], w13[e], w2[e])
+        f = fwd(x[toks], w13[e], w2[e])
         out = orc.expert_backward_mxfp8(dy[toks], x[toks], g, w13[e], w2[e], f)
         for i, (a, t, j) in enumerate(rows):
+            Y[a] += g[i] * f["O"][i]
             dX[a] += out["dXp"][i]
             dgate[a, j] = out["dgate"][i]
     dlog = orc.router_backward(r.gate[tokens], dgate, r.idx[tokens], r.E)
-    return {"dx": dX, "dgate": dgate, "dlogits": dlog}
+    return {"y": Y, "dx": dX, "dgate": dgate, "dlogits": dlog}
 
 
-def oracle_expert_wgrad_mx8(orc, inp: dict, r, e: int) -> dict:
+def oracle_expert_wgrad_mx8(orc, inp: dict, r, e: int, fwd=None) -> dict:
     """Weight gradients of expert e under the fp8_bwd backward (all of its rows)."""
+    fwd = fwd or orc.expert_forward
     a, b = int(r.offsets[e]), int(r.offsets[e + 1])
     w13, w2 = inp["w13"], inp["w2"]
     if b == a:
@@ -153,6 +159,6 @@ def oracle_expert_wgrad_mx8(orc, inp: dict, r, e: int) -> dict:
     flat = r.sorted_to_flat[a:b]
     tok = flat // r.k
     g = r.gate.reshape(-1)[flat]
-    f = orc.expert_forward(inp["x"][tok], w13[e], w2[e])
+    f = fwd(inp["x"][tok], w13[e], w2[e])
     out = orc.expert_backward_mxfp8(inp["dy"][tok], inp["x"][tok], g, w13[e], w2[e], f)
     return {"dw13": out["dW13"], "dw2": out["dW2"]}

@@ -209,3 +209,92 @@ def test_fp8_bwd_fullsize_sampled():
     print("[fp8_bwd] sampled errors", {k: f"{v:.2e}" for k, (v, _) in errs.items()}, flush=True)
     for key, (v, tol) in errs.items():
         assert v <= tol, (key, v)
+
+
+# ---------------------------------------------------------------------------
+# mxfp8 mode: MXFP8 forward GEMMs and the fp8_bwd backward.  With the forward
+# quantised too, the definition itself lands at 5-7e-2 from the exact fp64
+# layer at the full shape (more at the small shapes), so against the exact
+# layer the GPU must stay within the quantised oracle's own error plus the
+# bound against it.  Against the quantised oracle: G13 comes from the scaled
+# MFMA (~1e-5 of the sum of |products| per instruction), which moves a few
+# A and dG13 codes across E4M3 midpoints (y, dX, dW up to a few 1e-2);
+# dgate and dlogits see no extra quantisation step (~1e-5).
+# ---------------------------------------------------------------------------
+TOL_Q_MXFP8 = {"y": 3e-2, "dx": 4e-2, "dw13": 4e-2, "dw2": 4e-2, "dgate": 2e-3, "dlogits": 2e-3}
+
+
+def _compare_mxfp8_mode(dims, inp):
+    print(f"[mxfp8] dims={dims}", flush=True)
+    run = GpuRun(dims, inp)
+    run.run_all()
+    r = orc.route(inp["logits"], dims.k)
+    check_routing_exact(run.routing_np(), r)
+    Yq, stq = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r)
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    quant = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, stq)
+    exact = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    quant["y"], exact["y"] = Yq, Y
+    L = run.layer
+    got = {"y": to_np(L.y), "dx": to_np(L.dx), "dw13": to_np(L.dw13), "dw2": to_np(L.dw2),
+           "dgate": to_np(L.dgate), "dlogits": to_np(L.dlogits)}
+    e_q = {key: relerr(v, quant[key]) for key, v in got.items()}
+    e_x = {key: relerr(v, exact[key]) for key, v in got.items()}
+    e_qx = {key: relerr(quant[key], exact[key]) for key in got}
+    print("[mxfp8] vs quantised oracle", {k: f"{v:.2e}" for k, v in e_q.items()},
+          "; vs exact", {k: f"{v:.2e}" for k, v in e_x.items()},
+          "; quantised oracle vs exact", {k: f"{v:.2e}" for k, v in e_qx.items()}, flush=True)
+    for key in got:
+        assert e_q[key] <= TOL_Q_MXFP8[key], (key, e_q[key])
+        assert e_x[key] <= max(TOL_EXACT, e_qx[key] + TOL_Q_MXFP8[key]), (key, e_x[key])
+    for e in np.nonzero(r.counts == 0)[0]:
+        assert np.all(got["dw13"][e] == 0) and np.all(got["dw2"][e] == 0)
+    return run
+
+
+@pytest.mark.parametrize("dims,seed", [
+    (mi.LayerDims(T=256, H=256, I=128, E=8, k=2, dtype="bf16", mode="mxfp8"), 311),
+    (mi.LayerDims(T=700, H=384, I=256, E=16, k=4, dtype="bf16", mode="mxfp8"), 312),
+    (mi.LayerDims(T=777, H=512, I=256, E=32, k=8, dtype="bf16", skew=True, mode="mxfp8"), 313),
+])
+def test_mxfp8_mode_small(dims, seed):
+    _compare_mxfp8_mode(dims, mi.make_inputs(dims, seed))
+
+
+def test_mxfp8_mode_single_token():
+    d = mi.LayerDims(T=1, H=128, I=128, E=4, k=2, dtype="bf16", mode="mxfp8")
+    _compare_mxfp8_mode(d, mi.make_inputs(d, 314))
+
+
+def test_mxfp8_mode_fullsize_sampled():
+    """The Qwen3-30B-A3B shape in the mxfp8 mode, in the launch configuration
+    the benchmark times; sampled outputs against both oracles."""
+    import dataclasses
+    import torch
+    d = dataclasses.replace(mi.CONFIGS[2], mode="mxfp8")
+    print(f"[mxfp8] {mi.CONFIG_NAMES[2]}, mxfp8 mode", flush=True)
+    inp = mi.make_inputs(d, 2)
+    run = GpuRun(d, inp)
+    run.run_all()
+    L = run.layer
+    r = orc.route(inp["logits"], d.k)
+    check_routing_exact(run.routing_np(), r)
+    tokens = np.array([0, 5000, d.T - 1])
+    tt = torch.as_tensor(tokens, device="cuda")
+    q = oracle_token_rows_mx8(orc, inp, r, tokens, fwd=orc.expert_forward_mxfp8)
+    x = oracle_token_rows(orc, inp, r, tokens)
+    errs = {}
+    for key, t in (("y", L.y), ("dx", L.dx), ("dgate", L.dgate), ("dlogits", L.dlogits)):
+        v = to_np(t[tt])
+        errs[key + "/q"] = (relerr(v, q[key]), TOL_Q_MXFP8[key])
+        errs[key + "/exact"] = (relerr(v, x[key]), max(TOL_EXACT, relerr(q[key], x[key]) + TOL_Q_MXFP8[key]))
+    e = int(np.argsort(r.counts, kind="stable")[d.E // 2])
+    wq = oracle_expert_wgrad_mx8(orc, inp, r, e, fwd=orc.expert_forward_mxfp8)
+    wx = oracle_expert_wgrad(orc, inp, r, e)
+    for key, t in (("dw13", L.dw13[e]), ("dw2", L.dw2[e])):
+        v = to_np(t)
+        errs[f"{key}[{e}]/q"] = (relerr(v, wq[key]), TOL_Q_MXFP8[key])
+        errs[f"{key}[{e}]/exact"] = (relerr(v, wx[key]), max(TOL_EXACT, relerr(wq[key], wx[key]) + TOL_Q_MXFP8[key]))
+    print("[mxfp8] sampled errors", {k: f"{v:.2e}" for k, (v, _) in errs.items()}, flush=True)
+    for key, (v, tol) in errs.items():
+        assert v <= tol, (key, v)
