@@ -33,9 +33,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
 FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_a", "quant_w2", "gemm2", "combine"]
 BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
-BWD_KERNELS_FP8 = ["tile_table_b", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t", "quant_dg",
-                   "dgrad1", "unpermute_reduce", "router_bwd", "pad_offsets", "quant_dyt", "quant_agt", "wgrad2",
-                   "quant_dgt", "quant_xt", "wgrad1"]
+BWD_KERNELS_FP8 = ["tile_table_b", "pad_offsets", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t",
+                   "dgrad1", "unpermute_reduce", "router_bwd", "quant_dyt", "wgrad2", "quant_xt", "wgrad1"]
 
 
 class HipEvents:
@@ -76,8 +75,7 @@ def hbm_bytes(d):
     H, I, E, M, T = d.H, d.I, d.E, d.M, d.T
     return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4,
             "quant_w2t": q(E * H * I), "quant_w13t": q(E * 2 * I * H), "quant_dy": q(T * H),
-            "quant_dg": q(M * 2 * I), "quant_dyt": q(M * H), "quant_agt": q(M * I), "quant_dgt": q(M * 2 * I),
-            "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H), "quant_a": q4(M * I),
+            "quant_dyt": q(M * H), "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H), "quant_a": q4(M * I),
             "quant_w2": q(E * H * I)}
 
 

@@ -65,9 +65,8 @@ Sizes compute_sizes(const moe_dims* d) {
   s.r_partials = o; o += align_up(nblk * d->E * 4);
   s.r_bases = o;    o += align_up(nblk * d->E * 4);
   s.route_ws = o;
-  // fp8_bwd keeps the quantisers' inputs (G13, dG13, gate*A) in fp32
-  const size_t es_q = mx8_backward(d->mode) ? 4 : es;
-  s.saved = align_up(M * 2 * d->I * es_q);
+  // the MXFP8 backward keeps G13 in fp32: its derivatives are quantised unrounded
+  s.saved = align_up(M * 2 * d->I * (mx8_backward(d->mode) ? 4 : es));
   o = 0;
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
@@ -87,8 +86,10 @@ Sizes compute_sizes(const moe_dims* d) {
   s.b_tile_e = o; o += align_up(max_tiles_b * 4);
   s.b_tile_r = o; o += align_up(max_tiles_b * 4);
   s.b_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
-  s.b_dG13 = o;   o += align_up(M * 2 * d->I * es_q);
-  s.b_Ag = o;     o += align_up(M * d->I * es_q);
+  if (!mx8_backward(d->mode)) {   // the MXFP8 backward quantises them in the dgrad epilogue instead
+    s.b_dG13 = o; o += align_up(M * 2 * d->I * es);
+    s.b_Ag = o;   o += align_up(M * d->I * es);
+  }
   s.b_dXp = o;    o += align_up(M * d->H * es);
   s.b_part = o;   o += align_up((size_t)dgrad2_parts(d->mode, d->I) * M * 4);
   if (mx8_backward(d->mode)) {
@@ -171,10 +172,11 @@ constexpr int kForwardKernels = 4;    // tile table, GEMM1+SwiGLU, GEMM2, combin
 constexpr int kForwardKernelsMx8 = 8;
 inline int forward_kernels(int mode) { return mx8_forward(mode) ? kForwardKernelsMx8 : kForwardKernels; }
 constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13
-// fp8_bwd: tile table, quant W2^T, quant dY, dgrad W2, quant W13^T, quant dG13,
-// dgrad W13, unpermute, router, padded offsets, quant dY^T, quant (gA)^T,
-// wgrad W2, quant dG13^T, quant x^T, wgrad W13
-constexpr int kBackwardKernelsMx8 = 16;
+// MXFP8 backward: tile table, padded offsets, quant W2^T, quant dY, dgrad W2 +
+// dSwiGLU + quant dG13 (row and token blocks) and gate*A (token blocks),
+// quant W13^T, dgrad W13, unpermute, router, quant dY^T, wgrad W2, quant x^T,
+// wgrad W13
+constexpr int kBackwardKernelsMx8 = 13;
 inline int backward_kernels(int mode) { return mx8_backward(mode) ? kBackwardKernelsMx8 : kBackwardKernels; }
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
@@ -301,8 +303,9 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   LayerArgs a = base_args(dims, routing);
   a.x = x; a.w13 = w13; a.w2 = w2; a.dy = dy;
   a.G13 = const_cast<void*>(saved);
-  a.dG13 = at(ws, s.b_dG13);
-  a.Ag = at(ws, s.b_Ag);
+  const bool mx8 = mx8_backward(dims->mode);
+  a.dG13 = mx8 ? nullptr : at(ws, s.b_dG13);
+  a.Ag = mx8 ? nullptr : at(ws, s.b_Ag);
   a.dXp = at(ws, s.b_dXp);
   a.dgate_part = reinterpret_cast<float*>(at(ws, s.b_part));
   a.dw13 = dw13;
@@ -312,7 +315,6 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
   const int bm = bwd_row_tile_m(dims->mode);
-  const bool mx8 = mx8_backward(dims->mode);
   const Mx8Args q = mx8 ? mx8_args(s, ws) : Mx8Args{};
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
   const bf16_t* x16 = static_cast<const bf16_t*>(x);
@@ -324,6 +326,8 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   };
   step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream));
   if (mx8) {
+    // the dgrad epilogue of W2 places its token blocks at the padded offsets
+    if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, const_cast<int32_t*>(q.pad_off), stream));
     if (e == hipSuccess)
       step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, mut(q.qw2t), mut(q.sw2t), stream));
     if (e == hipSuccess) step(launch_mx_quant_rows(dy16, a.T, a.H, nullptr, 1, mut(q.qdy), mut(q.sdy), stream));
@@ -331,9 +335,6 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     if (e == hipSuccess)
       step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, mut(q.qw13t), mut(q.sw13t),
                                   stream));
-    if (e == hipSuccess)
-      step(launch_mx_quant_rows(static_cast<const float*>(a.dG13), a.M, 2 * a.I, nullptr, 1, mut(q.qdg),
-                                mut(q.sdg), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_DGRAD1, a, q, stream));
   } else {
     if (e == hipSuccess) step(gemm(bf16, KIND_DGRAD2, a, stream));
@@ -351,18 +352,11 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     step(launch_router_bwd(a.dgate_part, dgrad2_parts(dims->mode, a.I), a.f2s, a.gate, routing->topk_idx, a.T,
                            a.k, a.E, a.M, dgate, dlogits, stream));
   if (mx8) {
-    int32_t* pad = const_cast<int32_t*>(q.pad_off);
-    if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, pad, stream));
+    const int32_t* pad = q.pad_off;
     if (e == hipSuccess)
       step(launch_mx_quant_tokens_t(dy16, a.H, a.s2f, a.k, a.offsets, pad, a.E, q.Mp, mut(q.qdyt), mut(q.sdyt),
                                     stream));
-    if (e == hipSuccess)
-      step(launch_mx_quant_tokens_t(static_cast<const float*>(a.Ag), a.I, nullptr, 1, a.offsets, pad, a.E, q.Mp,
-                                    mut(q.qagt), mut(q.sagt), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_WGRAD2, a, q, stream));
-    if (e == hipSuccess)
-      step(launch_mx_quant_tokens_t(static_cast<const float*>(a.dG13), 2 * a.I, nullptr, 1, a.offsets, pad, a.E,
-                                    q.Mp, mut(q.qdgt), mut(q.sdgt), stream));
     if (e == hipSuccess)
       step(launch_mx_quant_tokens_t(x16, a.H, a.s2f, a.k, a.offsets, pad, a.E, q.Mp, mut(q.qxt), mut(q.sxt),
                                     stream));

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "moe_internal.h"
+#include "mx_codec.h"
 
 namespace moe {
 namespace gg {
@@ -154,8 +155,10 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       }
     }
   } else if constexpr (KIND == KIND_DGRAD2) {
-    // F32IO: G13 is read and dG13, gate*A are written in fp32 (inputs of the
-    // MXFP8 quantisers), else all three are bf16
+    static_assert(!F32IO, "the MXFP8 modes use dgrad2_epilogue_mx8");
+    const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
+    bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
+    bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
     // after the main loop's last barrier the A tiles are free: reused for the
     // cross-wave reduction of the gate-gradient partials
     float* s_part = reinterpret_cast<float*>(smem);
@@ -171,20 +174,12 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         const int n = n0 + wn * WN + 16 * j + ncol;
         if (n >= I) continue;
         const size_t o1 = (size_t)m * 2 * I + n, o3 = o1 + I;
-        float g1v[4], g3v[4];
-        if constexpr (F32IO) {
-          const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.G13) + o1);
-          const f32x4_t r3 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.G13) + o3);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) { g1v[v] = r1[v]; g3v[v] = r3[v]; }
-        } else {
-          const uint2 r1 = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(a.G13) + o1);
-          const uint2 r3 = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(a.G13) + o3);
-          g1v[0] = __uint_as_float(r1.x << 16); g1v[1] = __uint_as_float(r1.x & 0xFFFF0000u);
-          g1v[2] = __uint_as_float(r1.y << 16); g1v[3] = __uint_as_float(r1.y & 0xFFFF0000u);
-          g3v[0] = __uint_as_float(r3.x << 16); g3v[1] = __uint_as_float(r3.x & 0xFFFF0000u);
-          g3v[2] = __uint_as_float(r3.y << 16); g3v[3] = __uint_as_float(r3.y & 0xFFFF0000u);
-        }
+        const uint2 r1 = *reinterpret_cast<const uint2*>(G13 + o1);
+        const uint2 r3 = *reinterpret_cast<const uint2*>(G13 + o3);
+        const float g1v[4] = {__uint_as_float(r1.x << 16), __uint_as_float(r1.x & 0xFFFF0000u),
+                              __uint_as_float(r1.y << 16), __uint_as_float(r1.y & 0xFFFF0000u)};
+        const float g3v[4] = {__uint_as_float(r3.x << 16), __uint_as_float(r3.x & 0xFFFF0000u),
+                              __uint_as_float(r3.y << 16), __uint_as_float(r3.y & 0xFFFF0000u)};
         float d1[4], d3[4], ag[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -198,17 +193,9 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
           d3[v] = da * silu;
           ag[v] = g * av;
         }
-        if constexpr (F32IO) {
-          float* dG = static_cast<float*>(a.dG13);
-          st_out(dG + o1, f32x4_t{d1[0], d1[1], d1[2], d1[3]});
-          st_out(dG + o3, f32x4_t{d3[0], d3[1], d3[2], d3[3]});
-          st_out(static_cast<float*>(a.Ag) + (size_t)m * I + n, f32x4_t{ag[0], ag[1], ag[2], ag[3]});
-        } else {
-          bf16_t* dG = static_cast<bf16_t*>(a.dG13);
-          st_out(dG + o1, pack4(d1[0], d1[1], d1[2], d1[3]));
-          st_out(dG + o3, pack4(d3[0], d3[1], d3[2], d3[3]));
-          st_out(static_cast<bf16_t*>(a.Ag) + (size_t)m * I + n, pack4(ag[0], ag[1], ag[2], ag[3]));
-        }
+        st_out(dG13 + o1, pack4(d1[0], d1[1], d1[2], d1[3]));
+        st_out(dG13 + o3, pack4(d3[0], d3[1], d3[2], d3[3]));
+        st_out(Ag + (size_t)m * I + n, pack4(ag[0], ag[1], ag[2], ag[3]));
       }
       __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
     }
@@ -264,6 +251,182 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
           st_out<true>(out + (size_t)m * ld + n, *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
       }
     }
+  }
+}
+
+// Gate-gradient partials of one tile: lanes sharing a row, then the WGN waves
+// of a row block, in a fixed order.  `s_part` holds WGN * BM floats of LDS.
+template <class C>
+__device__ __forceinline__ void dgate_partials(const LayerArgs& a, float (&psum)[C::FM], float* s_part, int tid,
+                                               int lane, int wm, int wn, int m0, int mlim, int n0) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    psum[i] += __shfl_xor(psum[i], 16);
+    psum[i] += __shfl_xor(psum[i], 32);
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) s_part[wn * C::BM + wm * C::WM + 16 * i + lane] = psum[i];
+  }
+  __syncthreads();
+  for (int ml = tid; ml < C::BM; ml += C::NTHR) {
+    const int m = m0 + ml;
+    if (m < mlim) {
+      float p = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::WGN; ++w) p += s_part[w * C::BM + ml];
+      a.dgate_part[(size_t)(n0 / C::BN) * a.M + m] = p;
+    }
+  }
+}
+
+// Epilogue of the dgrad of W2 in the MXFP8 modes.  The gate-gradient
+// partials, the SwiGLU derivative and the gate fold are those of
+// gemm_epilogue (from the fp32 G13 these modes save), but instead of dG13 and
+// g*A the tile writes their MXFP8 operands of the following GEMMs:
+//   dG13 in row blocks of 32 along 2I (A operand of the dgrad of W13): the 4
+//     lanes that share a row reduce the block maximum, each lane stores the
+//     codes of its 4 consecutive columns;
+//   dG13 and g*A in token blocks of 32 (operands of the two weight
+//     gradients): the tile's 128 rows are one padded 128-token K tile of the
+//     expert (tiles start at the expert's first row, rows past its end count
+//     as zeros), the 16 lanes holding a column's block reduce its maximum, the
+//     codes are staged transposed in LDS and stored as whole 128-byte rows.
+// The values reaching the encoder are those the separate quantisers would
+// read, so the codes are the same.
+template <class C>
+__device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx8Args& q,
+                                                    f32x4_t (&acc)[C::FM][C::FN], void* smem, int tid, int lane,
+                                                    int wm, int wn, int e, int m0, int mlim, int n0) {
+  constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int NB = BM / 32;                                  // token blocks per tile
+  static_assert(BM == MX_KTILE && FM % 2 == 0 && FN % 2 == 0 && WM % 32 == 0, "tile = one padded K tile");
+  // staged code rows [column][BM tokens] padded to TS bytes: the 4 column
+  // groups of a fragment then fall on different LDS banks
+  constexpr int TS = BM + 16;
+  constexpr int T_DG = 1024, T_AG = T_DG + 2 * BN * TS, S_DG = T_AG + BN * TS, S_AG = S_DG + 2 * BN * NB;
+  static_assert(C::WGN * BM * 4 <= T_DG && S_AG + BN * NB <= C::SMEM_BYTES, "staging fits in the operand LDS");
+  uint8_t* lds = static_cast<uint8_t*>(smem);
+  const int I = a.I;
+  const int mrow = lane & 15, ncol = 4 * (lane >> 4);
+  const float* G13 = static_cast<const float*>(a.G13);
+  uint8_t* qdg = const_cast<uint8_t*>(q.qdg);
+  uint8_t* sdg = const_cast<uint8_t*>(q.sdg);
+  float psum[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) psum[i] = 0.f;
+
+#pragma unroll
+  for (int ip = 0; ip < FM / 2; ++ip) {
+#pragma unroll
+    for (int jp = 0; jp < FN / 2; ++jp) {
+      float d[3][2][2][4];   // [dG1, dG3, g*A][row block ii][column block jj][v]; zero outside the expert / I
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * ip + ii;
+        const int m = m0 + wm * WM + 16 * i + mrow;
+        const bool mv = m < mlim;
+        const float g = mv ? a.gate[a.s2f[m]] : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int n = n0 + wn * WN + 16 * (2 * jp + jj) + ncol;
+          const bool ok = mv && n < I;
+          f32x4_t g1 = {0.f, 0.f, 0.f, 0.f}, g3 = {0.f, 0.f, 0.f, 0.f};
+          if (ok) {
+            g1 = *reinterpret_cast<const f32x4_t*>(G13 + (size_t)m * 2 * I + n);
+            g3 = *reinterpret_cast<const f32x4_t*>(G13 + (size_t)m * 2 * I + I + n);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float dap = acc[i][2 * jp + jj][v];
+            const float s = sigmoid_f32(g1[v]);
+            const float silu = g1[v] * s;
+            const float av = silu * g3[v];
+            if (ok) psum[i] += dap * av;
+            const float da = g * dap;
+            d[0][ii][jj][v] = ok ? da * g3[v] * s * (1.f + g1[v] * (1.f - s)) : 0.f;
+            d[1][ii][jj][v] = ok ? da * silu : 0.f;
+            d[2][ii][jj][v] = ok ? g * av : 0.f;
+          }
+        }
+      }
+      // row blocks of dG13 (32 columns = fragments 2jp, 2jp+1; 4 lanes per row)
+      const int c0 = n0 + wn * WN + 32 * jp;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int m = m0 + wm * WM + 16 * (2 * ip + ii) + mrow;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float amax = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(d[h][ii][jj][v]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const int X = mx_scale_exp(amax);
+          if (m < mlim && c0 < I) {
+            const size_t row = (size_t)m * 2 * I + h * I + c0;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+              *reinterpret_cast<uint32_t*>(qdg + row + 16 * jj + ncol) =
+                  mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X);
+            if (ncol == 0) sdg[(size_t)m * (2 * I / 32) + (h * I + c0) / 32] = (uint8_t)(X + 127);
+          }
+        }
+      }
+      // token blocks (32 rows = fragments 2ip, 2ip+1; 16 lanes per column), staged in LDS
+      const int tl = wm * WM + 32 * ip + mrow;                 // tile token of row block 0
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+        for (int h = 0; h < 3; ++h) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float amax = fmaxf(fabsf(d[h][0][jj][v]), fabsf(d[h][1][jj][v]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            amax = fmaxf(amax, __shfl_xor(amax, 4));
+            amax = fmaxf(amax, __shfl_xor(amax, 8));
+            const int X = mx_scale_exp(amax);
+            const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(d[h][0][jj][v], -X),
+                                                                         ldexpf(d[h][1][jj][v], -X), 0, false);
+            const int cl = wn * WN + 16 * (2 * jp + jj) + ncol + v;   // tile column
+            uint8_t* t = lds + (h == 2 ? T_AG + cl * TS : T_DG + (h * BN + cl) * TS);
+            t[tl] = (uint8_t)(w & 0xFFu);
+            t[tl + 16] = (uint8_t)((w >> 8) & 0xFFu);
+            if (mrow == 0)
+              lds[(h == 2 ? S_AG + cl * NB : S_DG + (h * BN + cl) * NB) + wm * (WM / 32) + ip] = (uint8_t)(X + 127);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one 2x2 block of fragments live at a time
+    }
+  }
+
+  dgate_partials<C>(a, psum, reinterpret_cast<float*>(lds), tid, lane, wm, wn, m0, mlim, n0);   // ends with a barrier
+
+  // the staged token blocks -> the transposed operands, whole rows of the K tile
+  const size_t Mp = (size_t)q.Mp;
+  const size_t p0 = (size_t)q.pad_off[e] + (size_t)(m0 - a.offsets[e]);
+  uint8_t* qdgt = const_cast<uint8_t*>(q.qdgt);
+  uint8_t* sdgt = const_cast<uint8_t*>(q.sdgt);
+  uint8_t* qagt = const_cast<uint8_t*>(q.qagt);
+  uint8_t* sagt = const_cast<uint8_t*>(q.sagt);
+  for (int idx = tid; idx < 3 * BN * (BM / 16); idx += NTHR) {
+    const int col = idx / (BM / 16), ch = idx % (BM / 16);   // col < 2 BN: dG1 | dG3, then g*A
+    const int c = n0 + col % BN;
+    if (c >= I) continue;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + (col < 2 * BN ? T_DG + col * TS : T_AG + (col - 2 * BN) * TS) + 16 * ch);
+    uint8_t* dst = col < 2 * BN ? qdgt + (size_t)(col < BN ? c : I + c) * Mp : qagt + (size_t)c * Mp;
+    *reinterpret_cast<u32x4_t*>(dst + p0 + 16 * ch) = v;
+  }
+  for (int col = tid; col < 3 * BN; col += NTHR) {
+    const int c = n0 + col % BN;
+    if (c >= I) continue;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(lds + (col < 2 * BN ? S_DG + col * NB : S_AG + (col - 2 * BN) * NB));
+    uint8_t* dst = col < 2 * BN ? sdgt + (size_t)(col < BN ? c : I + c) * (Mp / 32) : sagt + (size_t)c * (Mp / 32);
+    *reinterpret_cast<uint32_t*>(dst + p0 / 32) = v;
   }
 }
 

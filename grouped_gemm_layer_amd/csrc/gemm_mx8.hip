@@ -26,8 +26,10 @@
 // that row (lane layout checked against a CPU product on the device).  The
 // MFMA's first operand is the B tile, so lane l holds D[n = 4*(l/16) + v][m =
 // l%16], the layout the shared epilogues expect.  The epilogue of the dgrad
-// of W2 reads the fp32 G13 saved in this mode and writes dG13 and gate*A in
-// fp32, so the quantisers see them unrounded.
+// of W2 reads the fp32 G13 saved in these modes and quantises dG13 and
+// gate*A from fp32 registers straight into the MXFP8 operands of the three
+// GEMMs that follow (row blocks for the dgrad of W13, token blocks for both
+// weight gradients).
 //
 // LDS stage: A codes [BM][128], B codes [BN][128] (16-byte chunks XOR-swizzled
 // by row & 7, conflict-free two-chunk reads), then A scales [BM][4] and B
@@ -268,7 +270,10 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
 
-  gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim);
+  if constexpr (KIND == KIND_DGRAD2)
+    gg::dgrad2_epilogue_mx8<C>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
+  else
+    gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim);
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).  The

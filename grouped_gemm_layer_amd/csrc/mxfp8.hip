@@ -16,44 +16,9 @@
 // operand's GEMM-K (contiguous).  The scaling by 2^-X is exact (ldexp) and the
 // E4M3 rounding is the hardware conversion (nearest, ties to even), so the
 // codes are those of the exact definition for the same inputs.
-#include "moe_internal.h"
+#include "mx_codec.h"
 
 namespace moe {
-
-// X from the bits of amax (finite, >= 0): amax = (1 + f) 2^(eb-127) and
-// 448 = 1.75 * 2^8, so X = eb - 135 when f <= 0.75, else eb - 134.
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-  const uint32_t b = __float_as_uint(amax);
-  const int eb = (int)(b >> 23);
-  int X;
-  if (eb != 0) {
-    X = eb - 127 - ((b & 0x7FFFFFu) <= 0x600000u ? 8 : 7);
-  } else {                              // zero or an fp32 subnormal
-    if (b == 0) return -127;
-    int ea;
-    const float m = frexpf(amax, &ea);  // amax = m 2^ea, m in [0.5, 1)
-    X = (2.f * m <= 1.75f) ? ea - 9 : ea - 8;
-  }
-  return min(max(X, -127), 127);
-}
-
-// 32 values -> 32 codes packed into 8 words (element i in byte i%4 of word
-// i/4), returns the E8M0 byte.  v / 2^X is exact (ldexp); the hardware
-// conversion rounds to the nearest E4M3FN value, ties to even, and keeps the
-// sign of zero; |v / 2^X| <= 448 by the choice of X, so nothing overflows.
-__device__ __forceinline__ uint32_t mx_quant_block(const float (&v)[32], uint32_t (&packed)[8]) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int X = mx_scale_exp(amax);
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w], -X), ldexpf(v[4 * w + 1], -X), 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w + 2], -X), ldexpf(v[4 * w + 3], -X), word, true);
-    packed[w] = (uint32_t)word;
-  }
-  return (uint32_t)(X + 127);
-}
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4 r, float* out) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};

@@ -140,10 +140,10 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, con
  * quantised along that GEMM's reduction dimension as moe_mxfp8_quantize
  * describes: dy and W2 along H, dG13 and W13 along 2I, and for the weight
  * gradients dy, gate*A, dG13 and x along the tokens of each expert in blocks
- * that start at the expert's first row (moe_mxfp8_quantize_grouped).  The
- * quantisers see fp32 values of dG13 and gate*A (in this mode the forward
- * saves G13 in fp32); dgate, the SwiGLU derivative and the router gradient
- * use the unquantised forward state. */
+ * that start at the expert's first row (moe_mxfp8_quantize_grouped).  dG13
+ * and gate*A are quantised in fp32, inside the dgrad of W2 that produces
+ * them (in this mode the forward saves G13 in fp32); dgate, the SwiGLU
+ * derivative and the router gradient use the unquantised forward state. */
 moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, const void* w13,
                         const void* w2, const moe_routing* routing, const void* saved,
                         void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
@@ -160,11 +160,11 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  *             SwiGLU, quantise A, quantise W2, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
  *             unpermute-reduce, router backward, wgrad W2, wgrad W13
- *   backward, MOE_MODE_FP8_BWD and MOE_MODE_MXFP8: tile table, quantise W2^T, quantise dy,
- *             dgrad W2 + SwiGLU derivative, quantise W13^T, quantise dG13,
- *             dgrad W13, unpermute-reduce, router backward, padded expert
- *             offsets, quantise dy^T, quantise (gate*A)^T, wgrad W2,
- *             quantise dG13^T, quantise x^T, wgrad W13 */
+ *   backward, MOE_MODE_FP8_BWD and MOE_MODE_MXFP8: tile table, padded
+ *             expert offsets, quantise W2^T, quantise dy, dgrad W2 + SwiGLU
+ *             derivative + quantise dG13 and gate*A, quantise W13^T, dgrad
+ *             W13, unpermute-reduce, router backward, quantise dy^T, wgrad
+ *             W2, quantise x^T, wgrad W13 */
 moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                              const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events, int n_events);
