@@ -96,6 +96,117 @@ __device__ __forceinline__ void st_out(P* p, V v) {
   else *reinterpret_cast<V*>(p) = v;
 }
 
+// Cross-lane reductions without LDS traffic (DPP and the gfx950 row swaps).
+// The maxima are taken over the bit patterns of non-negative floats, which
+// order like the values.
+// maximum over the 16 lanes of each row (lanes 16r .. 16r+15)
+__device__ __forceinline__ uint32_t umax_row16(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  return v;
+}
+// maximum over the lanes l, l^16, l^32, l^48
+__device__ __forceinline__ uint32_t umax_rows4(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)r[0], (uint32_t)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+// sum over the lanes l, l^16, l^32, l^48 (every lane gets the same value)
+__device__ __forceinline__ float fsum_rows4(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// sum over the 32 lanes of each half wave (every lane gets the same value)
+__device__ __forceinline__ float fsum_lanes32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// Gate-gradient partials of one tile: lanes sharing a row, then the WGN waves
+// of a row block, in a fixed order.  `s_part` holds WGN * BM floats of LDS.
+template <class C>
+__device__ __forceinline__ void dgate_partials(const LayerArgs& a, float (&psum)[C::FM], float* s_part, int tid,
+                                               int lane, int wm, int wn, int m0, int mlim, int n0) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) psum[i] = fsum_rows4(psum[i]);
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) s_part[wn * C::BM + wm * C::WM + 16 * i + lane] = psum[i];
+  }
+  __syncthreads();
+  for (int ml = tid; ml < C::BM; ml += C::NTHR) {
+    const int m = m0 + ml;
+    if (m < mlim) {
+      float p = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::WGN; ++w) p += s_part[w * C::BM + ml];
+      a.dgate_part[(size_t)(n0 / C::BN) * a.M + m] = p;
+    }
+  }
+}
+
+// Writes one output tile of the row kinds through LDS, so that every store
+// instruction covers whole rows: a lane holds 4 consecutive columns of 16
+// rows (pieces spread over 16 lines), the copy-out stores 16 bytes per lane
+// along rows.  `val(i, j)` returns the 4 values of the wave's row block i and
+// fragment j (0 <= j < FJ), tile columns wn*16*FJ + 16 j + 4*(lane/16) .. +3,
+// as 4 packed bf16 (u32x2_t) or 4 floats (f32x4_t).  Row m, tile column t
+// goes to out[m * ld + c0 + t] for m < mlim and c0 + t < clim (clim a
+// multiple of the 16-byte chunk).  The tile passes in chunks of CH rows when
+// it exceeds the operand LDS.  The caller has freed the LDS (barrier after
+// the main loop); the function ends with a barrier, so the LDS may be
+// reused after it.
+template <class C, int FJ, class T, class Val>
+__device__ __forceinline__ void staged_store(void* smem, Val&& val, T* out, size_t ld, int m0, int mlim, int c0,
+                                             int clim, int tid, int lane, int wm, int wn) {
+  using V = decltype(val(0, 0));
+  constexpr int BM = C::BM, WM = C::WM, FM = C::FM, NTHR = C::NTHR;
+  constexpr int VB = (int)sizeof(V);                      // bytes of 4 values
+  static_assert(VB == 4 * (int)sizeof(T), "values match the output type");
+  constexpr int TW = C::WGN * 16 * FJ;                    // tile width (elements)
+  constexpr int RB = TW * (VB / 4);                       // bytes per tile row
+  constexpr int NQ = RB / 16, EQ = 16 / (VB / 4);         // 16-byte chunks per row, elements per chunk
+  constexpr int CH0 = C::SMEM_BYTES / RB;
+  constexpr int CH = CH0 >= BM ? BM : CH0 >= 64 ? 64 : CH0 >= 32 ? 32 : 16;
+  static_assert(CH * RB <= C::SMEM_BYTES && BM % CH == 0 && CH % 16 == 0 && WM % 16 == 0,
+                "row chunk must fit in the operand LDS");
+  uint8_t* s = static_cast<uint8_t*>(smem);
+  const int mrow = lane & 15, ncol = 4 * (lane >> 4);
+  auto off = [&](int row, int q) { return row * RB + ((q ^ (row % NQ)) << 4); };
+#pragma unroll
+  for (int ch = 0; ch < BM / CH; ++ch) {
+    if (ch > 0) __syncthreads();                          // the previous chunk has been read out
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if ((wm * WM + 16 * i) / CH != ch) continue;        // a 16-row block lies in one chunk
+      const int row = wm * WM + 16 * i + mrow - ch * CH;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int byte = (wn * 16 * FJ + 16 * j + ncol) * (VB / 4);
+        *reinterpret_cast<V*>(s + off(row, byte >> 4) + (byte & 15)) = val(i, j);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < CH * NQ; c += NTHR) {
+      const int row = c / NQ, q = c % NQ;
+      const int m = m0 + ch * CH + row, n = c0 + EQ * q;
+      if (m < mlim && n < clim)
+        *reinterpret_cast<u32x4_t*>(out + (size_t)m * ld + n) = *reinterpret_cast<const u32x4_t*>(s + off(row, q));
+    }
+  }
+  __syncthreads();
+}
+
 // Epilogue of one output tile.  acc[i][j][v] holds C[m][n] for
 //   m = m0 + wm*WM + 16 i + lane%16,  n = n0 + wn*WN + 16 j + 4*(lane/16) + v
 // (for the SwiGLU kind the first FN/2 column blocks are G1 and the rest the
@@ -111,112 +222,111 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
   const int ncol = 4 * (lane >> 4);   // first of 4 consecutive columns
 
   if constexpr (KIND == KIND_FWD1) {
-    bf16_t* Aout = static_cast<bf16_t*>(a.A);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WM + 16 * i + mrow;
-      if (m >= mlim) continue;
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j) {
-        const int c = n0 + wn * (WN / 2) + 16 * j + ncol;
-        if (c >= I) continue;
-        const f32x4_t g1 = acc[i][j], g3 = acc[i][j + FN / 2];
-        float av[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = g1[v] * sigmoid_f32(g1[v]) * g3[v];
-        if (a.g13_f32) {   // saved state kept in fp32 (MXFP8 backward quantises from it)
-          float* G13 = static_cast<float*>(a.G13);
-          st_out(G13 + (size_t)m * 2 * I + c, g1);
-          st_out(G13 + (size_t)m * 2 * I + I + c, g3);
-        } else {
-          bf16_t* G13 = static_cast<bf16_t*>(a.G13);
-          st_out(G13 + (size_t)m * 2 * I + c, pack4(g1[0], g1[1], g1[2], g1[3]));
-          st_out(G13 + (size_t)m * 2 * I + I + c, pack4(g3[0], g3[1], g3[2], g3[3]));
-        }
-        if constexpr (F32IO)   // the input of the MXFP8 quantiser of A
-          st_out(reinterpret_cast<float*>(a.A) + (size_t)m * I + c, f32x4_t{av[0], av[1], av[2], av[3]});
-        else
-          st_out(Aout + (size_t)m * I + c, pack4(av[0], av[1], av[2], av[3]));
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
+    // the first FN/2 fragments hold G1 columns, the rest the matching G3 columns
+    constexpr int FH = FN / 2;
+    const int c0 = n0;
+    const size_t ld13 = (size_t)2 * I;
+    auto gv = [&](int i, int j) { const f32x4_t g = acc[i][j]; return pack4(g[0], g[1], g[2], g[3]); };
+    auto av = [&](int i, int j) {
+      const f32x4_t g1 = acc[i][j], g3 = acc[i][j + FH];
+      return f32x4_t{g1[0] * sigmoid_f32(g1[0]) * g3[0], g1[1] * sigmoid_f32(g1[1]) * g3[1],
+                     g1[2] * sigmoid_f32(g1[2]) * g3[2], g1[3] * sigmoid_f32(g1[3]) * g3[3]};
+    };
+    if (a.g13_f32) {   // saved state kept in fp32 (the MXFP8 backward quantises from it)
+      float* G13 = static_cast<float*>(a.G13);
+      staged_store<C, FH>(smem, [&](int i, int j) { return acc[i][j]; }, G13, ld13, m0, mlim, c0, I, tid, lane, wm, wn);
+      staged_store<C, FH>(smem, [&](int i, int j) { return acc[i][j + FH]; }, G13 + I, ld13, m0, mlim, c0, I, tid,
+                          lane, wm, wn);
+    } else {
+      bf16_t* G13 = static_cast<bf16_t*>(a.G13);
+      staged_store<C, FH>(smem, gv, G13, ld13, m0, mlim, c0, I, tid, lane, wm, wn);
+      staged_store<C, FH>(smem, [&](int i, int j) { return gv(i, j + FH); }, G13 + I, ld13, m0, mlim, c0, I, tid,
+                          lane, wm, wn);
     }
+    if constexpr (F32IO)   // the input of the MXFP8 quantiser of A
+      staged_store<C, FH>(smem, av, static_cast<float*>(a.A), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
+    else
+      staged_store<C, FH>(smem, [&](int i, int j) { const f32x4_t v = av(i, j); return pack4(v[0], v[1], v[2], v[3]); },
+                          static_cast<bf16_t*>(a.A), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
     bf16_t* out = static_cast<bf16_t*>(KIND == KIND_FWD2 ? a.O : a.dXp);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WM + 16 * i + mrow;
-      if (m >= mlim) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * WN + 16 * j + ncol;
-        if (n >= nlim) continue;
-        const f32x4_t v = acc[i][j];
-        st_out(out + (size_t)m * H + n, pack4(v[0], v[1], v[2], v[3]));
-      }
-    }
+    staged_store<C, FN>(smem, [&](int i, int j) { const f32x4_t v = acc[i][j]; return pack4(v[0], v[1], v[2], v[3]); },
+                        out, (size_t)H, m0, mlim, n0, nlim, tid, lane, wm, wn);
   } else if constexpr (KIND == KIND_DGRAD2) {
     static_assert(!F32IO, "the MXFP8 modes use dgrad2_epilogue_mx8");
+    // dA' = acc passes through LDS in fp32, CH rows at a time; then each
+    // thread takes 8 consecutive columns of one row: coalesced 16-byte loads
+    // of G1 and G3, stores of dG1, dG3 and g*A, and the row's gate-gradient
+    // partial summed over the 32 lanes that hold the row (fixed order).
+    constexpr int NQ4 = BN / 4;                            // 16-byte fp32 chunks per row
+    constexpr int TPR = BN / 8;                            // threads per row
+    static_assert(TPR == 32 && NTHR % TPR == 0, "one row per half wave");
+    constexpr int CH0 = C::SMEM_BYTES / (BN * 4);
+    constexpr int CH = CH0 >= BM ? BM : CH0 >= 64 ? 64 : CH0 >= 32 ? 32 : 16;
+    static_assert(CH * BN * 4 <= C::SMEM_BYTES && BM % CH == 0 && CH % 16 == 0, "fp32 row chunk must fit");
     const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
     bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
     bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
-    // after the main loop's last barrier the A tiles are free: reused for the
-    // cross-wave reduction of the gate-gradient partials
-    float* s_part = reinterpret_cast<float*>(smem);
-    float psum[FM];
+    float* s_acc = reinterpret_cast<float*>(smem);
+    auto off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ4)) << 2); };
+    auto unpack = [](uint32_t w, float& lo, float& hi) {
+      lo = __uint_as_float(w << 16);
+      hi = __uint_as_float(w & 0xFFFF0000u);
+    };
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      psum[i] = 0.f;
-      const int m = m0 + wm * WM + 16 * i + mrow;
-      if (m >= mlim) continue;
-      const float g = a.gate[a.s2f[m]];
+    for (int ch = 0; ch < BM / CH; ++ch) {
+      if (ch > 0) __syncthreads();                         // the previous chunk has been read
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * WN + 16 * j + ncol;
-        if (n >= I) continue;
-        const size_t o1 = (size_t)m * 2 * I + n, o3 = o1 + I;
-        const uint2 r1 = *reinterpret_cast<const uint2*>(G13 + o1);
-        const uint2 r3 = *reinterpret_cast<const uint2*>(G13 + o3);
-        const float g1v[4] = {__uint_as_float(r1.x << 16), __uint_as_float(r1.x & 0xFFFF0000u),
-                              __uint_as_float(r1.y << 16), __uint_as_float(r1.y & 0xFFFF0000u)};
-        const float g3v[4] = {__uint_as_float(r3.x << 16), __uint_as_float(r3.x & 0xFFFF0000u),
-                              __uint_as_float(r3.y << 16), __uint_as_float(r3.y & 0xFFFF0000u)};
-        float d1[4], d3[4], ag[4];
+      for (int i = 0; i < FM; ++i) {
+        if ((wm * WM + 16 * i) / CH != ch) continue;
+        const int row = wm * WM + 16 * i + mrow - ch * CH;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float dap = acc[i][j][v];
-          const float s = sigmoid_f32(g1v[v]);
-          const float silu = g1v[v] * s;
-          const float av = silu * g3v[v];
-          psum[i] += dap * av;
-          const float da = g * dap;
-          d1[v] = da * g3v[v] * s * (1.f + g1v[v] * (1.f - s));
-          d3[v] = da * silu;
-          ag[v] = g * av;
-        }
-        st_out(dG13 + o1, pack4(d1[0], d1[1], d1[2], d1[3]));
-        st_out(dG13 + o3, pack4(d3[0], d3[1], d3[2], d3[3]));
-        st_out(Ag + (size_t)m * I + n, pack4(ag[0], ag[1], ag[2], ag[3]));
+        for (int j = 0; j < FN; ++j)
+          *reinterpret_cast<f32x4_t*>(&s_acc[off(row, (wn * WN + 16 * j + ncol) >> 2)]) = acc[i][j];
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep one 16-row block's values live at a time
-    }
-    // lanes sharing a row, then the WGN waves of a row block, in a fixed order
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      psum[i] += __shfl_xor(psum[i], 16);
-      psum[i] += __shfl_xor(psum[i], 32);
-    }
-    if (lane < 16) {
+      for (int c = tid; c < CH * TPR; c += NTHR) {
+        const int row = c / TPR, q = c % TPR;
+        const int m = m0 + ch * CH + row, n = n0 + 8 * q;
+        const bool ok = m < mlim && n < I;
+        const f32x4_t da0 = *reinterpret_cast<const f32x4_t*>(&s_acc[off(row, 2 * q)]);
+        const f32x4_t da1 = *reinterpret_cast<const f32x4_t*>(&s_acc[off(row, 2 * q + 1)]);
+        float part = 0.f;
+        if (ok) {
+          const float g = a.gate[a.s2f[m]];
+          const size_t o1 = (size_t)m * 2 * I + n;
+          const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(G13 + o1);
+          const u32x4_t r3 = *reinterpret_cast<const u32x4_t*>(G13 + o1 + I);
+          float g1[8], g3[8], dap[8], d1[8], d3[8], ag[8];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) s_part[wn * BM + wm * WM + 16 * i + lane] = psum[i];
-    }
-    __syncthreads();
-    for (int ml = tid; ml < BM; ml += NTHR) {
-      const int m = m0 + ml;
-      if (m < mlim) {
-        float p = 0.f;
+          for (int w = 0; w < 4; ++w) {
+            unpack(r1[w], g1[2 * w], g1[2 * w + 1]);
+            unpack(r3[w], g3[2 * w], g3[2 * w + 1]);
+            dap[w] = da0[w];
+            dap[4 + w] = da1[w];
+          }
 #pragma unroll
-        for (int w = 0; w < C::WGN; ++w) p += s_part[w * BM + ml];
-        a.dgate_part[(size_t)(n0 / BN) * a.M + m] = p;
+          for (int v = 0; v < 8; ++v) {
+            const float sg = sigmoid_f32(g1[v]);
+            const float silu = g1[v] * sg;
+            const float av = silu * g3[v];
+            part += dap[v] * av;
+            const float da = g * dap[v];
+            d1[v] = da * g3[v] * sg * (1.f + g1[v] * (1.f - sg));
+            d3[v] = da * silu;
+            ag[v] = g * av;
+          }
+          *reinterpret_cast<u32x4_t*>(dG13 + o1) = u32x4_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]),
+                                                            pack_bf16x2(d1[4], d1[5]), pack_bf16x2(d1[6], d1[7])};
+          *reinterpret_cast<u32x4_t*>(dG13 + o1 + I) = u32x4_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3]),
+                                                                pack_bf16x2(d3[4], d3[5]), pack_bf16x2(d3[6], d3[7])};
+          *reinterpret_cast<u32x4_t*>(Ag + (size_t)m * I + n) =
+              u32x4_t{pack_bf16x2(ag[0], ag[1]), pack_bf16x2(ag[2], ag[3]), pack_bf16x2(ag[4], ag[5]),
+                      pack_bf16x2(ag[6], ag[7])};
+        }
+        part = fsum_lanes32(part);                         // the 32 lanes of this row
+        if ((lane & 31) == 0 && m < mlim) a.dgate_part[(size_t)(n0 / BN) * a.M + m] = part;
       }
     }
   } else {   // wgrad: fp32 output of one expert, staged through LDS so each
@@ -250,32 +360,6 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         if (m < mlim && n < nlim)
           st_out<true>(out + (size_t)m * ld + n, *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
       }
-    }
-  }
-}
-
-// Gate-gradient partials of one tile: lanes sharing a row, then the WGN waves
-// of a row block, in a fixed order.  `s_part` holds WGN * BM floats of LDS.
-template <class C>
-__device__ __forceinline__ void dgate_partials(const LayerArgs& a, float (&psum)[C::FM], float* s_part, int tid,
-                                               int lane, int wm, int wn, int m0, int mlim, int n0) {
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    psum[i] += __shfl_xor(psum[i], 16);
-    psum[i] += __shfl_xor(psum[i], 32);
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) s_part[wn * C::BM + wm * C::WM + 16 * i + lane] = psum[i];
-  }
-  __syncthreads();
-  for (int ml = tid; ml < C::BM; ml += C::NTHR) {
-    const int m = m0 + ml;
-    if (m < mlim) {
-      float p = 0.f;
-#pragma unroll
-      for (int w = 0; w < C::WGN; ++w) p += s_part[w * C::BM + ml];
-      a.dgate_part[(size_t)(n0 / C::BN) * a.M + m] = p;
     }
   }
 }
@@ -357,14 +441,12 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
         const int m = m0 + wm * WM + 16 * (2 * ip + ii) + mrow;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float amax = 0.f;
+          uint32_t amax = 0;
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(d[h][ii][jj][v]));
-          amax = fmaxf(amax, __shfl_xor(amax, 16));
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
-          const int X = mx_scale_exp(amax);
+            for (int v = 0; v < 4; ++v) amax = max(amax, abs_bits(d[h][ii][jj][v]));
+          const int X = mx_scale_exp(__uint_as_float(umax_rows4(amax)));
           if (m < mlim && c0 < I) {
             const size_t row = (size_t)m * 2 * I + h * I + c0;
 #pragma unroll
@@ -383,12 +465,8 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
         for (int h = 0; h < 3; ++h) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            float amax = fmaxf(fabsf(d[h][0][jj][v]), fabsf(d[h][1][jj][v]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            amax = fmaxf(amax, __shfl_xor(amax, 8));
-            const int X = mx_scale_exp(amax);
+            const uint32_t amax = umax_row16(max(abs_bits(d[h][0][jj][v]), abs_bits(d[h][1][jj][v])));
+            const int X = mx_scale_exp(__uint_as_float(amax));
             const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(d[h][0][jj][v], -X),
                                                                          ldexpf(d[h][1][jj][v], -X), 0, false);
             const int cl = wn * WN + 16 * (2 * jp + jj) + ncol + v;   // tile column
