@@ -31,7 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 operands)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
-FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_a", "quant_w2", "gemm2", "combine"]
+FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_w2", "gemm2", "combine"]
 BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
 BWD_KERNELS_FP8 = ["tile_table_b", "pad_offsets", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t",
                    "dgrad1", "unpermute_reduce", "router_bwd", "quant_dyt", "wgrad2", "quant_xt", "wgrad1"]
@@ -71,11 +71,10 @@ def hbm_bytes(d):
     codes + one scale byte per 32 codes)."""
     rows = d.M * d.H * 2 + d.T * d.H * 2
     q = lambda n: n * 2 + n + n // 32            # read bf16, write codes + scales
-    q4 = lambda n: n * 4 + n + n // 32           # read fp32, write codes + scales
     H, I, E, M, T = d.H, d.I, d.E, d.M, d.T
     return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4,
             "quant_w2t": q(E * H * I), "quant_w13t": q(E * 2 * I * H), "quant_dy": q(T * H),
-            "quant_dyt": q(M * H), "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H), "quant_a": q4(M * I),
+            "quant_dyt": q(M * H), "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H),
             "quant_w2": q(E * H * I)}
 
 

@@ -71,7 +71,9 @@ Sizes compute_sizes(const moe_dims* d) {
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
   s.f_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
-  s.f_A = o;      o += align_up(M * d->I * (mx8_forward(d->mode) ? 4 : es));   // fp32 when it is quantised
+  if (!mx8_forward(d->mode)) {   // the mxfp8 forward quantises A in the epilogue instead
+    s.f_A = o; o += align_up(M * d->I * es);
+  }
   s.f_O = o;      o += align_up(M * d->H * es);
   if (mx8_forward(d->mode)) {
     const size_t T = d->T, H = d->H, I = d->I, E = d->E;
@@ -168,8 +170,8 @@ struct Marks {
 // kernels per call, in launch order
 constexpr int kRouteKernels = 4;      // topk+gate, histogram, scan, scatter
 constexpr int kForwardKernels = 4;    // tile table, GEMM1+SwiGLU, GEMM2, combine
-// mxfp8: tile table, quant x, quant W13, GEMM1+SwiGLU, quant A, quant W2, GEMM2, combine
-constexpr int kForwardKernelsMx8 = 8;
+// mxfp8: tile table, quant x, quant W13, GEMM1+SwiGLU+quant A, quant W2, GEMM2, combine
+constexpr int kForwardKernelsMx8 = 7;
 inline int forward_kernels(int mode) { return mx8_forward(mode) ? kForwardKernelsMx8 : kForwardKernels; }
 constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13
 // MXFP8 backward: tile table, padded offsets, quant W2^T, quant dY, dgrad W2 +
@@ -238,7 +240,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   a.x = x; a.w13 = w13; a.w2 = w2;
   a.G13 = saved;
   a.g13_f32 = mx8_backward(dims->mode);
-  a.A = at(ws, s.f_A);
+  a.A = mx8_forward(dims->mode) ? nullptr : at(ws, s.f_A);
   a.O = at(ws, s.f_O);
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.f_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.f_tile_r));
@@ -257,6 +259,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     q.qx = u8(s.f_qx);     q.sx = u8(s.f_sx);
     q.qw13 = u8(s.f_qw13); q.sw13 = u8(s.f_sw13);
     q.qa = u8(s.f_qa);     q.sa = u8(s.f_sa);
+    a.q_a = u8(s.f_qa);    a.q_sa = u8(s.f_sa);
     q.qw2 = u8(s.f_qw2);   q.sw2 = u8(s.f_sw2);
     const bf16_t* x16 = static_cast<const bf16_t*>(x);
     if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));
@@ -264,9 +267,6 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
       step(launch_mx_quant_rows(static_cast<const bf16_t*>(w13), a.E * 2 * a.I, a.H, nullptr, 1, u8(s.f_qw13),
                                 u8(s.f_sw13), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
-    if (e == hipSuccess)
-      step(launch_mx_quant_rows(static_cast<const float*>(a.A), a.M, a.I, nullptr, 1, u8(s.f_qa), u8(s.f_sa),
-                                stream));
     if (e == hipSuccess)
       step(launch_mx_quant_rows(static_cast<const bf16_t*>(w2), a.E * a.H, a.I, nullptr, 1, u8(s.f_qw2),
                                 u8(s.f_sw2), stream));

@@ -107,6 +107,25 @@ __device__ __forceinline__ uint32_t umax_row16(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
   return v;
 }
+// umax_row16 over a whole array, one DPP step at a time across all elements
+// (independent chains back to back need no wait states between steps)
+template <int CTRL, int N0, int N1, int N2>
+__device__ __forceinline__ void umax_dpp_step(uint32_t (&v)[N0][N1][N2]) {
+#pragma unroll
+  for (int a = 0; a < N0; ++a)
+#pragma unroll
+    for (int b = 0; b < N1; ++b)
+#pragma unroll
+      for (int c = 0; c < N2; ++c)
+        v[a][b][c] = max(v[a][b][c], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[a][b][c], CTRL, 0xF, 0xF, false));
+}
+template <int N0, int N1, int N2>
+__device__ __forceinline__ void row16_umax_steps(uint32_t (&v)[N0][N1][N2]) {
+  umax_dpp_step<0xB1>(v);    // quad_perm 1,0,3,2
+  umax_dpp_step<0x4E>(v);    // quad_perm 2,3,0,1
+  umax_dpp_step<0x141>(v);   // row_half_mirror
+  umax_dpp_step<0x140>(v);   // row_mirror
+}
 // maximum over the lanes l, l^16, l^32, l^48
 __device__ __forceinline__ uint32_t umax_rows4(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -243,9 +262,33 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       staged_store<C, FH>(smem, [&](int i, int j) { return gv(i, j + FH); }, G13 + I, ld13, m0, mlim, c0, I, tid,
                           lane, wm, wn);
     }
-    if constexpr (F32IO)   // the input of the MXFP8 quantiser of A
-      staged_store<C, FH>(smem, av, static_cast<float*>(a.A), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
-    else
+    if constexpr (F32IO) {
+      // MXFP8 operand of the GEMM W2 straight from fp32: blocks of 32 along I
+      // are fragment pairs (2jb, 2jb+1); the 4 lanes sharing a row reduce the
+      // block maximum with row swaps, codes leave through LDS along rows and
+      // the scale byte from the lane holding the block's first columns
+      static_assert(FH % 2 == 0, "a block of 32 columns = two fragments");
+      const auto r_sa = make_rsrc(a.q_sa, (uint32_t)a.M * (I / 32));
+      int X[FM][FH / 2];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 16 * i + mrow;
+#pragma unroll
+        for (int jb = 0; jb < FH / 2; ++jb) {
+          const f32x4_t v0 = av(i, 2 * jb), v1 = av(i, 2 * jb + 1);
+          uint32_t amax = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = max(amax, max(abs_bits(v0[v]), abs_bits(v1[v])));
+          X[i][jb] = mx_scale_exp(__uint_as_float(umax_rows4(amax)));
+          const int cb = c0 + wn * 16 * FH + 32 * jb;   // first column of the block
+          if (ncol == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X[i][jb] + 127), r_sa,
+                                                 (m < mlim && cb < I) ? (uint32_t)m * (I / 32) + cb / 32 : OOB, 0, 0);
+        }
+      }
+      staged_store<C, FH>(smem, [&](int i, int j) { const f32x4_t v = av(i, j); return mx_pack4(v[0], v[1], v[2], v[3], X[i][j / 2]); },
+                          static_cast<uint8_t*>(a.q_a), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
+    } else
       staged_store<C, FH>(smem, [&](int i, int j) { const f32x4_t v = av(i, j); return pack4(v[0], v[1], v[2], v[3]); },
                           static_cast<bf16_t*>(a.A), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
@@ -394,8 +437,10 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
   const int I = a.I;
   const int mrow = lane & 15, ncol = 4 * (lane >> 4);
   const float* G13 = static_cast<const float*>(a.G13);
-  uint8_t* qdg = const_cast<uint8_t*>(q.qdg);
-  uint8_t* sdg = const_cast<uint8_t*>(q.sdg);
+  // row codes and scales of dG13 by buffer stores: offsets past the end (OOB)
+  // are dropped, which masks rows past the expert and columns past I
+  const auto r_qdg = make_rsrc(q.qdg, (uint32_t)a.M * 2 * I);
+  const auto r_sdg = make_rsrc(q.sdg, (uint32_t)a.M * 2 * I / 32);
   float psum[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) psum[i] = 0.f;
@@ -409,16 +454,19 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * ip + ii;
         const int m = m0 + wm * WM + 16 * i + mrow;
-        const bool mv = m < mlim;
-        const float g = mv ? a.gate[a.s2f[m]] : 0.f;
+        const int mc = min(m, mlim - 1);                     // rows past the expert: in-bounds reads, zeroed
+        const float g = a.gate[a.s2f[mc]];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int n = n0 + wn * WN + 16 * (2 * jp + jj) + ncol;
-          const bool ok = mv && n < I;
-          f32x4_t g1 = {0.f, 0.f, 0.f, 0.f}, g3 = {0.f, 0.f, 0.f, 0.f};
-          if (ok) {
-            g1 = *reinterpret_cast<const f32x4_t*>(G13 + (size_t)m * 2 * I + n);
-            g3 = *reinterpret_cast<const f32x4_t*>(G13 + (size_t)m * 2 * I + I + n);
+          const bool ok = m < mlim && n < I;
+          const size_t o = (size_t)mc * 2 * I + min(n, I - 4);
+          f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(G13 + o);
+          f32x4_t g3 = *reinterpret_cast<const f32x4_t*>(G13 + o + I);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {   // zero G13 outside the tile: every derived value is then zero
+            g1[v] = ok ? g1[v] : 0.f;
+            g3[v] = ok ? g3[v] : 0.f;
           }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -426,11 +474,11 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
             const float s = sigmoid_f32(g1[v]);
             const float silu = g1[v] * s;
             const float av = silu * g3[v];
-            if (ok) psum[i] += dap * av;
+            psum[i] += dap * av;
             const float da = g * dap;
-            d[0][ii][jj][v] = ok ? da * g3[v] * s * (1.f + g1[v] * (1.f - s)) : 0.f;
-            d[1][ii][jj][v] = ok ? da * silu : 0.f;
-            d[2][ii][jj][v] = ok ? g * av : 0.f;
+            d[0][ii][jj][v] = da * g3[v] * s * (1.f + g1[v] * (1.f - s));
+            d[1][ii][jj][v] = da * silu;
+            d[2][ii][jj][v] = g * av;
           }
         }
       }
@@ -447,26 +495,35 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
 #pragma unroll
             for (int v = 0; v < 4; ++v) amax = max(amax, abs_bits(d[h][ii][jj][v]));
           const int X = mx_scale_exp(__uint_as_float(umax_rows4(amax)));
-          if (m < mlim && c0 < I) {
-            const size_t row = (size_t)m * 2 * I + h * I + c0;
+          const bool ok = m < mlim && c0 < I;
+          const uint32_t row = (uint32_t)m * 2 * I + h * I + c0;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-              *reinterpret_cast<uint32_t*>(qdg + row + 16 * jj + ncol) =
-                  mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X);
-            if (ncol == 0) sdg[(size_t)m * (2 * I / 32) + (h * I + c0) / 32] = (uint8_t)(X + 127);
-          }
+          for (int jj = 0; jj < 2; ++jj)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X), r_qdg,
+                ok ? row + 16 * jj + ncol : OOB, 0, 0);
+          if (ncol == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), r_sdg, ok ? row / 32 : OOB, 0, 0);
         }
       }
-      // token blocks (32 rows = fragments 2ip, 2ip+1; 16 lanes per column), staged in LDS
+      // token blocks (32 rows = fragments 2ip, 2ip+1; 16 lanes per column), staged in LDS.
+      // The 24 maxima of this sub-block advance through the DPP steps together.
       const int tl = wm * WM + 32 * ip + mrow;                 // tile token of row block 0
+      uint32_t am[2][3][4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int h = 0; h < 3; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) am[jj][h][v] = max(abs_bits(d[h][0][jj][v]), abs_bits(d[h][1][jj][v]));
+      row16_umax_steps(am);
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
         for (int h = 0; h < 3; ++h) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t amax = umax_row16(max(abs_bits(d[h][0][jj][v]), abs_bits(d[h][1][jj][v])));
-            const int X = mx_scale_exp(__uint_as_float(amax));
+            const int X = mx_scale_exp(__uint_as_float(am[jj][h][v]));
             const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(d[h][0][jj][v], -X),
                                                                          ldexpf(d[h][1][jj][v], -X), 0, false);
             const int cl = wn * WN + 16 * (2 * jp + jj) + ncol + v;   // tile column

@@ -44,7 +44,8 @@ template <> struct ElemTraits<bf16_t> {
 //   A = SiLU(g1) * g3,  SiLU(z) = z * sigmoid(z)
 //   dg1 = dA * g3 * s * (1 + g1 (1 - s)),  dg3 = dA * SiLU(g1)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// logistic sigmoid; the reciprocal is the hardware one (1 ulp), not an IEEE division
+__device__ __forceinline__ float sigmoid_f32(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------
 // Problem description handed to every GEMM launcher.
@@ -69,6 +70,8 @@ struct LayerArgs {
   int g13_f32;                    // G13 stored in fp32 (fp8_bwd mode) instead of the activation type
   void* G13;                      // [M,2I]  (saved)
   void* A;                        // [M,I]
+  uint8_t* q_a;                   // mxfp8 mode: MXFP8 codes of A [M,I] (written by the GEMM W13 epilogue)
+  uint8_t* q_sa;                  //   and their scales [M,I/32]
   void* O;                        // [M,H]
   // backward intermediates / outputs (fp32 in fp8_bwd mode)
   void* dG13;                     // [M,2I]

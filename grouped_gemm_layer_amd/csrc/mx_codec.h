@@ -11,19 +11,15 @@
 namespace moe {
 
 // X from the bits of amax (finite, >= 0): amax = (1 + f) 2^(eb-127) and
-// 448 = 1.75 * 2^8, so X = eb - 135 when f <= 0.75, else eb - 134.
+// 448 = 1.75 * 2^8, so X = eb - 135 when f <= 0.75, else eb - 134; adding
+// 0x1FFFFF to the bits carries into the exponent exactly when f > 0.75.  A
+// zero or subnormal amax is first scaled by 2^64 (exact), which makes it
+// normal; zero then lands below -127 and clamps there.  Branch-free.
 __device__ __forceinline__ int mx_scale_exp(float amax) {
   const uint32_t b = __float_as_uint(amax);
-  const int eb = (int)(b >> 23);
-  int X;
-  if (eb != 0) {
-    X = eb - 127 - ((b & 0x7FFFFFu) <= 0x600000u ? 8 : 7);
-  } else {                              // zero or an fp32 subnormal
-    if (b == 0) return -127;
-    int ea;
-    const float m = frexpf(amax, &ea);  // amax = m 2^ea, m in [0.5, 1)
-    X = (2.f * m <= 1.75f) ? ea - 9 : ea - 8;
-  }
+  const bool sub = b < 0x800000u;
+  const uint32_t u = sub ? __float_as_uint(amax * 18446744073709551616.f) : b;   // amax * 2^64
+  const int X = (int)((u + 0x1FFFFFu) >> 23) - (sub ? 135 + 64 : 135);
   return min(max(X, -127), 127);
 }
 

@@ -97,9 +97,11 @@ __global__ __launch_bounds__(512) void pad_offsets_kernel(const int32_t* __restr
 //     output [E][F][Kd]; grid.y = Kd / MX_KTILE.
 // A tile of MX_KTILE rows x QT_F features is staged in LDS as fp32 with
 // coalesced 16-byte row loads; thread (f, q) then quantises feature f over
-// the 32 rows of block q and stores its 32 codes and one scale byte.
+// the 32 rows of block q, and the codes and scales leave through LDS along
+// the output rows.
 constexpr int QT_F = 64;            // features per tile
 constexpr int QT_LD = QT_F + 4;     // LDS row stride (floats): rows stay 16-byte aligned
+constexpr int QT_CLD = MX_KTILE + 16;   // LDS row stride of the staged codes (bytes)
 
 template <typename T, bool GROUPED>
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ src, int F,
@@ -110,6 +112,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
                                                          uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) float s_tile[MX_KTILE * QT_LD];
   __shared__ int s_src[MX_KTILE];       // source row of each tile row, -1 = padding
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[QT_F * QT_CLD];   // codes [feature][tile row]
+  __shared__ __attribute__((aligned(4))) uint8_t s_scales[QT_F * 4];        // scales [feature][block]
   const int f0 = blockIdx.x * QT_F;
   const int p0 = MX_KTILE * blockIdx.y;
   size_t out_base = 0, sc_base = 0;
@@ -170,18 +174,33 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
   }
   __syncthreads();
 
-  // one feature x one block of 32 rows per thread (a wave = 64 features of one block)
+  // one feature x one block of 32 rows per thread (a wave = 64 features of one
+  // block); codes and scales are staged in LDS so that the stores run along
+  // the output rows (8 lanes per 128-byte row of the tile)
   const int f = threadIdx.x % QT_F, q = threadIdx.x / QT_F;
-  if (f0 + f >= F) return;
-  float v[32];
+  {
+    float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = s_tile[(32 * q + i) * QT_LD + f];
-  uint32_t packed[8];
-  const uint32_t sc = mx_quant_block(v, packed);
-  uint4* o = reinterpret_cast<uint4*>(codes + out_base + (size_t)(f0 + f) * ld_out + p0 + 32 * q);
-  o[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  o[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  scales[sc_base + (size_t)(f0 + f) * (ld_out / 32) + p0 / 32 + q] = (uint8_t)sc;
+    for (int i = 0; i < 32; ++i) v[i] = s_tile[(32 * q + i) * QT_LD + f];
+    uint32_t packed[8];
+    const uint32_t sc = mx_quant_block(v, packed);
+    uint4* d = reinterpret_cast<uint4*>(&s_codes[f * QT_CLD + 32 * q]);
+    d[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    d[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    s_scales[f * 4 + q] = (uint8_t)sc;
+  }
+  __syncthreads();
+  constexpr int CPT = MX_KTILE / 16;             // 16-byte chunks per output row of the tile
+#pragma unroll
+  for (int i = threadIdx.x; i < QT_F * CPT; i += 256) {
+    const int ff = i / CPT, ch = i % CPT;
+    if (f0 + ff < F)
+      *reinterpret_cast<uint4*>(codes + out_base + (size_t)(f0 + ff) * ld_out + p0 + 16 * ch) =
+          *reinterpret_cast<const uint4*>(&s_codes[ff * QT_CLD + 16 * ch]);
+  }
+  if (threadIdx.x < QT_F && f0 + threadIdx.x < F)
+    *reinterpret_cast<uint32_t*>(scales + sc_base + (size_t)(f0 + threadIdx.x) * (ld_out / 32) + p0 / 32) =
+        *reinterpret_cast<const uint32_t*>(&s_scales[threadIdx.x * 4]);
 }
 
 template <typename T>

@@ -114,7 +114,7 @@ moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routin
  * MOE_MODE_MXFP8 (Prime Mega MoE news page, "How does the fused kernel
  * work?": BF16 and MXFP8 precisions): both GEMMs read their operands as
  * MXFP8 quantised along K as moe_mxfp8_quantize describes (x and W13 along H,
- * A and W2 along I; A is quantised from its fp32 value); SwiGLU, the combine
+ * A and W2 along I; A is quantised from its fp32 value inside GEMM W13); SwiGLU, the combine
  * and y stay as above.  Its backward is the MOE_MODE_FP8_BWD backward. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                        const moe_routing* routing, void* y, void* saved,
@@ -157,7 +157,7 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  * (MOE_ERR_NULL / MOE_ERR_DIMS otherwise).  Kernel order:
  *   forward : tile table, GEMM W13 + SwiGLU, GEMM W2, combine
  *   forward, MOE_MODE_MXFP8: tile table, quantise x, quantise W13, GEMM W13 +
- *             SwiGLU, quantise A, quantise W2, GEMM W2, combine
+ *             SwiGLU + quantise A, quantise W2, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
  *             unpermute-reduce, router backward, wgrad W2, wgrad W13
  *   backward, MOE_MODE_FP8_BWD and MOE_MODE_MXFP8: tile table, padded
