@@ -35,6 +35,8 @@ FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_
 BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
 BWD_KERNELS_FP8 = ["tile_table_b", "pad_offsets", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t",
                    "dgrad1", "unpermute_reduce", "router_bwd", "quant_dyt", "wgrad2", "quant_xt", "wgrad1"]
+# mxfp8 mode: the forward quantises each weight both ways, the backward reuses W2^T and W13^T codes
+BWD_KERNELS_MXFP8 = [n for n in BWD_KERNELS_FP8 if n not in ("quant_w2t", "quant_w13t")]
 
 
 class HipEvents:
@@ -71,11 +73,12 @@ def hbm_bytes(d):
     codes + one scale byte per 32 codes)."""
     rows = d.M * d.H * 2 + d.T * d.H * 2
     q = lambda n: n * 2 + n + n // 32            # read bf16, write codes + scales
+    q2 = lambda n: n * 2 + 2 * (n + n // 32)     # read bf16, write both layouts (mxfp8 weights)
     H, I, E, M, T = d.H, d.I, d.E, d.M, d.T
     return {"combine": rows + d.M * 8, "unpermute_reduce": rows + d.M * 4,
             "quant_w2t": q(E * H * I), "quant_w13t": q(E * 2 * I * H), "quant_dy": q(T * H),
-            "quant_dyt": q(M * H), "quant_xt": q(M * H), "quant_x": q(T * H), "quant_w13": q(E * 2 * I * H),
-            "quant_w2": q(E * H * I)}
+            "quant_dyt": q(M * H), "quant_xt": q(M * H), "quant_x": q(T * H),
+            "quant_w13": q2(E * 2 * I * H), "quant_w2": q2(E * H * I)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -194,7 +197,7 @@ def main():
     fp8_bwd = d.run_mode in ("fp8_bwd", "mxfp8")
     fp8_fwd = d.run_mode == "mxfp8"
     fwd_names = FWD_KERNELS_MX8 if fp8_fwd else FWD_KERNELS
-    bwd_names = BWD_KERNELS_FP8 if fp8_bwd else BWD_KERNELS
+    bwd_names = BWD_KERNELS_MXFP8 if fp8_fwd else BWD_KERNELS_FP8 if fp8_bwd else BWD_KERNELS
     assert nf == len(fwd_names) and nb == len(bwd_names)
     fp8_gemms = (("gemm1_swiglu", "gemm2") if fp8_fwd else ()) + \
         (("dgrad2_dswiglu", "dgrad1", "wgrad2", "wgrad1") if fp8_bwd else ())

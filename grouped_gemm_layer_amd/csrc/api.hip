@@ -27,6 +27,8 @@ struct Sizes {
   size_t b_tile_e, b_tile_r, b_tile_x, b_dG13, b_Ag, b_dXp, b_part;
   // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
   size_t Mp;
+  // mxfp8: the transposed weight operands of the backward, kept in `saved` by the forward
+  size_t sv_qw13t, sv_sw13t, sv_qw2t, sv_sw2t;
   size_t q_pad, q_dy, s_dy, q_w2t, s_w2t, q_dg, s_dg, q_w13t, s_w13t;
   size_t q_dyt, s_dyt, q_agt, s_agt, q_dgt, s_dgt, q_xt, s_xt;
 };
@@ -67,6 +69,13 @@ Sizes compute_sizes(const moe_dims* d) {
   s.route_ws = o;
   // the MXFP8 backward keeps G13 in fp32: its derivatives are quantised unrounded
   s.saved = align_up(M * 2 * d->I * (mx8_backward(d->mode) ? 4 : es));
+  if (mx8_forward(d->mode)) {   // weights are quantised both ways once, in the forward
+    const size_t w13 = (size_t)d->E * 2 * d->I * d->H, w2 = (size_t)d->E * d->H * d->I;
+    s.sv_qw13t = s.saved; s.saved += align_up(w13);
+    s.sv_sw13t = s.saved; s.saved += align_up(w13 / 32);
+    s.sv_qw2t = s.saved;  s.saved += align_up(w2);
+    s.sv_sw2t = s.saved;  s.saved += align_up(w2 / 32);
+  }
   o = 0;
   s.f_tile_e = o; o += align_up(max_tiles * 4);
   s.f_tile_r = o; o += align_up(max_tiles * 4);
@@ -101,9 +110,11 @@ Sizes compute_sizes(const moe_dims* d) {
     auto take = [&](size_t& at_, size_t bytes) { at_ = o; o += align_up(bytes); };
     take(s.q_pad, (E + 1) * 4);
     take(s.q_dy, T * H);          take(s.s_dy, T * H / 32);
-    take(s.q_w2t, E * I * H);     take(s.s_w2t, E * I * H / 32);
+    if (!mx8_forward(d->mode)) {   // else in `saved`
+      take(s.q_w2t, E * I * H);     take(s.s_w2t, E * I * H / 32);
+      take(s.q_w13t, E * H * 2 * I); take(s.s_w13t, E * H * 2 * I / 32);
+    }
     take(s.q_dg, M * 2 * I);      take(s.s_dg, M * 2 * I / 32);
-    take(s.q_w13t, E * H * 2 * I); take(s.s_w13t, E * H * 2 * I / 32);
     take(s.q_dyt, H * Mp);        take(s.s_dyt, H * Mp / 32);
     take(s.q_agt, I * Mp);        take(s.s_agt, I * Mp / 32);
     take(s.q_dgt, 2 * I * Mp);    take(s.s_dgt, 2 * I * Mp / 32);
@@ -137,15 +148,21 @@ inline hipError_t gemm(bool bf16, GemmKind kind, const LayerArgs& a, hipStream_t
   return bf16 ? launch_gemm_bf16(kind, a, s) : launch_gemm_fp32(kind, a, s);
 }
 
-Mx8Args mx8_args(const Sizes& s, void* ws) {
+Mx8Args mx8_args(const moe_dims* d, const Sizes& s, void* ws, const void* saved) {
   auto u8 = [&](size_t off) { return reinterpret_cast<const uint8_t*>(at(ws, off)); };
+  auto sv = [&](size_t off) { return static_cast<const uint8_t*>(saved) + off; };
   Mx8Args q{};
   q.pad_off = reinterpret_cast<const int32_t*>(at(ws, s.q_pad));
   q.Mp = (int)s.Mp;
   q.qdy = u8(s.q_dy);     q.sdy = u8(s.s_dy);
-  q.qw2t = u8(s.q_w2t);   q.sw2t = u8(s.s_w2t);
   q.qdg = u8(s.q_dg);     q.sdg = u8(s.s_dg);
-  q.qw13t = u8(s.q_w13t); q.sw13t = u8(s.s_w13t);
+  if (mx8_forward(d->mode)) {
+    q.qw2t = sv(s.sv_qw2t);   q.sw2t = sv(s.sv_sw2t);
+    q.qw13t = sv(s.sv_qw13t); q.sw13t = sv(s.sv_sw13t);
+  } else {
+    q.qw2t = u8(s.q_w2t);   q.sw2t = u8(s.s_w2t);
+    q.qw13t = u8(s.q_w13t); q.sw13t = u8(s.s_w13t);
+  }
   q.qdyt = u8(s.q_dyt);   q.sdyt = u8(s.s_dyt);
   q.qagt = u8(s.q_agt);   q.sagt = u8(s.s_agt);
   q.qdgt = u8(s.q_dgt);   q.sdgt = u8(s.s_dgt);
@@ -179,7 +196,10 @@ constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W
 // quant W13^T, dgrad W13, unpermute, router, quant dY^T, wgrad W2, quant x^T,
 // wgrad W13
 constexpr int kBackwardKernelsMx8 = 13;
-inline int backward_kernels(int mode) { return mx8_backward(mode) ? kBackwardKernelsMx8 : kBackwardKernels; }
+// MOE_MODE_MXFP8: the same without the two weight quantisers (the forward saved W2^T and W13^T codes)
+inline int backward_kernels(int mode) {
+  return mx8_forward(mode) ? kBackwardKernelsMx8 - 2 : mx8_backward(mode) ? kBackwardKernelsMx8 : kBackwardKernels;
+}
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
@@ -263,13 +283,14 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     q.qw2 = u8(s.f_qw2);   q.sw2 = u8(s.f_sw2);
     const bf16_t* x16 = static_cast<const bf16_t*>(x);
     if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));
+    auto svp = [&](size_t off) { return static_cast<uint8_t*>(saved) + off; };
     if (e == hipSuccess)
-      step(launch_mx_quant_rows(static_cast<const bf16_t*>(w13), a.E * 2 * a.I, a.H, nullptr, 1, u8(s.f_qw13),
-                                u8(s.f_sw13), stream));
+      step(launch_mx_quant_both(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, svp(s.sv_qw13t),
+                                svp(s.sv_sw13t), u8(s.f_qw13), u8(s.f_sw13), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
     if (e == hipSuccess)
-      step(launch_mx_quant_rows(static_cast<const bf16_t*>(w2), a.E * a.H, a.I, nullptr, 1, u8(s.f_qw2),
-                                u8(s.f_sw2), stream));
+      step(launch_mx_quant_both(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, svp(s.sv_qw2t), svp(s.sv_sw2t),
+                                u8(s.f_qw2), u8(s.f_sw2), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
   } else {
     if (e == hipSuccess) step(gemm(bf16, KIND_FWD1, a, stream));
@@ -315,7 +336,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
   a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
   const int bm = bwd_row_tile_m(dims->mode);
-  const Mx8Args q = mx8 ? mx8_args(s, ws) : Mx8Args{};
+  const Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
   const bf16_t* x16 = static_cast<const bf16_t*>(x);
   // activation-gradient chain first; the weight gradients do not feed it
@@ -328,11 +349,12 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   if (mx8) {
     // the dgrad epilogue of W2 places its token blocks at the padded offsets
     if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, const_cast<int32_t*>(q.pad_off), stream));
-    if (e == hipSuccess)
+    const bool wq = !mx8_forward(dims->mode);   // mxfp8: the forward saved W2^T and W13^T codes
+    if (e == hipSuccess && wq)
       step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, mut(q.qw2t), mut(q.sw2t), stream));
     if (e == hipSuccess) step(launch_mx_quant_rows(dy16, a.T, a.H, nullptr, 1, mut(q.qdy), mut(q.sdy), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_DGRAD2, a, q, stream));
-    if (e == hipSuccess)
+    if (e == hipSuccess && wq)
       step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, mut(q.qw13t), mut(q.sw13t),
                                   stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_DGRAD1, a, q, stream));

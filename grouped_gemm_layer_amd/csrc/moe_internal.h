@@ -166,6 +166,12 @@ hipError_t launch_mx_quant_rows(const T* src, int R, int K, const int32_t* s2f, 
                                 uint8_t* scales, hipStream_t s);
 hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s);
+// Both MXFP8 copies of dense weights [E][Kd][N] from one read: transposed
+// ([E][N][Kd], blocks of 32 along Kd, as launch_mx_quant_cols_t) and row-wise
+// ([E*Kd][N], blocks of 32 along N, as launch_mx_quant_rows).  N % 64 == 0,
+// Kd % 128 == 0.
+hipError_t launch_mx_quant_both(const bf16_t* src, int E, int Kd, int N, uint8_t* codes_t, uint8_t* scales_t,
+                                uint8_t* codes_r, uint8_t* scales_r, hipStream_t s);
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t s);
 template <typename T>   // T = bf16_t or float
 hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,

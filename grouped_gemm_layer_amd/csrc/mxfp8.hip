@@ -92,30 +92,50 @@ __global__ __launch_bounds__(512) void pad_offsets_kernel(const int32_t* __restr
 //   GROUPED: source rows r of the expert-sorted order (read as
 //     src[s2f[r] / k] when s2f is given: gathered x / dY rows); expert e's
 //     rows go to output columns pad_off[e] .., the gap up to pad_off[e+1]
-//     holds zero codes; grid.y = padded tiles of MX_KTILE columns.
-//   dense: blockIdx.z = expert of a [E][Kd][F] source, rows e*Kd + p;
-//     output [E][F][Kd]; grid.y = Kd / MX_KTILE.
+//     holds zero codes; n_ptiles = padded tiles of MX_KTILE columns.
+//   dense: tile expert e (n_e of them) of a [E][Kd][F] source, rows e*Kd + p;
+//     output [E][F][Kd]; n_ptiles = Kd / MX_KTILE.
 // A tile of MX_KTILE rows x QT_F features is staged in LDS as fp32 with
 // coalesced 16-byte row loads; thread (f, q) then quantises feature f over
 // the 32 rows of block q, and the codes and scales leave through LDS along
 // the output rows.
 constexpr int QT_F = 64;            // features per tile
-constexpr int QT_LD = QT_F + 4;     // LDS row stride (floats): rows stay 16-byte aligned
+// LDS row stride of the source tile (elements of the source type, which the
+// tile keeps: bf16 is staged as is): rows stay 16-byte aligned
+template <typename T> constexpr int qt_ld() { return QT_F + 16 / (int)sizeof(T); }
 constexpr int QT_CLD = MX_KTILE + 16;   // LDS row stride of the staged codes (bytes)
+constexpr int QT_RLD = QT_F + 16;       // LDS row stride of the staged row-wise codes (bytes)
 
-template <typename T, bool GROUPED>
+template <typename T, bool GROUPED, bool ROWS = false>
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ src, int F,
                                                          const int32_t* __restrict__ s2f, int k,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ pad_off, int E, int Kd,
                                                          int ld_out, uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales) {
-  __shared__ __attribute__((aligned(16))) float s_tile[MX_KTILE * QT_LD];
+                                                         uint8_t* __restrict__ scales,
+                                                         int n_ptiles, int n_e,
+                                                         uint8_t* __restrict__ row_codes = nullptr,
+                                                         uint8_t* __restrict__ row_scales = nullptr) {
+  constexpr int QT_LD = qt_ld<T>();
+  __shared__ __attribute__((aligned(16))) T s_tile[MX_KTILE * QT_LD];
   __shared__ int s_src[MX_KTILE];       // source row of each tile row, -1 = padding
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[QT_F * QT_CLD];   // codes [feature][tile row]
   __shared__ __attribute__((aligned(4))) uint8_t s_scales[QT_F * 4];        // scales [feature][block]
-  const int f0 = blockIdx.x * QT_F;
-  const int p0 = MX_KTILE * blockIdx.y;
+  // row-wise codes / scales of the tile (ROWS only)
+  __shared__ __attribute__((aligned(16))) uint8_t s_rcodes[ROWS ? MX_KTILE * QT_RLD : 16];
+  __shared__ __attribute__((aligned(4))) uint8_t s_rscales[ROWS ? MX_KTILE * 2 : 4];
+  // 1-D grid of nf x np x ne tiles (features fastest).  Dense sources are
+  // renumbered so that each XCD (blocks are dealt round-robin to the 8 XCDs)
+  // takes a contiguous run of tiles: neighbouring feature tiles, whose
+  // row-wise output shares lines, then meet in one L2 (measured faster; the
+  // gathered token tiles run faster in launch order)
+  const int per_xcd = gridDim.x / 8;
+  const int L = GROUPED ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  const int nf = (F + QT_F - 1) / QT_F;
+  if (L >= nf * n_ptiles * n_e) return;
+  const int tf = L % nf, tp = (L / nf) % n_ptiles, te = L / (nf * n_ptiles);
+  const int f0 = tf * QT_F;
+  const int p0 = MX_KTILE * tp;
   size_t out_base = 0, sc_base = 0;
   if constexpr (GROUPED) {
     if (p0 >= pad_off[E]) return;       // uniform over the block
@@ -129,7 +149,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
       s_src[threadIdx.x] = (r < offsets[lo + 1]) ? (s2f ? s2f[r] / k : r) : -1;
     }
   } else {
-    const int e = blockIdx.z;
+    const int e = te;
     if (threadIdx.x < MX_KTILE) s_src[threadIdx.x] = e * Kd + p0 + threadIdx.x;
     out_base = (size_t)e * F * ld_out;
     sc_base = (size_t)e * F * (ld_out / 32);
@@ -151,28 +171,52 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
                                    : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      float v[EPC];
-      if constexpr (sizeof(T) == 2) {
-        unpack_bf16x8(raw[p], v);
-      } else {
-        v[0] = __uint_as_float(raw[p].x); v[1] = __uint_as_float(raw[p].y);
-        v[2] = __uint_as_float(raw[p].z); v[3] = __uint_as_float(raw[p].w);
-      }
-      float* d = &s_tile[(r0 + p * RPP) * QT_LD + c * EPC];
-#pragma unroll
-      for (int i = 0; i < EPC; i += 4) *reinterpret_cast<f32x4_t*>(d + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
-    }
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<uint4*>(&s_tile[(r0 + p * RPP) * QT_LD + c * EPC]) = raw[p];
   } else {
     for (int r = r0; r < MX_KTILE; r += RPP) {
       const int sr = s_src[r];
 #pragma unroll
       for (int i = 0; i < EPC; ++i)
-        s_tile[r * QT_LD + c * EPC + i] =
-            (sr >= 0 && fc + i < F) ? ElemTraits<T>::load(src + (size_t)sr * F + fc + i) : 0.f;
+        s_tile[r * QT_LD + c * EPC + i] = (sr >= 0 && fc + i < F) ? src[(size_t)sr * F + fc + i] : T(0);
     }
   }
   __syncthreads();
+
+  if constexpr (ROWS) {
+    // the same tile quantised along its rows as well (dense sources, F a
+    // multiple of QT_F): thread = one tile row x one block of 32 features
+    static_assert(!GROUPED && 2 * MX_KTILE == 256, "two row blocks per tile row");
+    const int r = threadIdx.x % MX_KTILE, b = threadIdx.x / MX_KTILE;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; i += EPC) {
+      const uint4 t = *reinterpret_cast<const uint4*>(&s_tile[r * QT_LD + 32 * b + i]);
+      if constexpr (sizeof(T) == 2) {
+        unpack_bf16x8(t, v + i);
+      } else {
+        v[i] = __uint_as_float(t.x); v[i + 1] = __uint_as_float(t.y);
+        v[i + 2] = __uint_as_float(t.z); v[i + 3] = __uint_as_float(t.w);
+      }
+    }
+    uint32_t packed[8];
+    const uint32_t sc = mx_quant_block(v, packed);
+    // staged in LDS, then stored along the rows: 4 lanes per 64-byte row piece
+    uint4* d = reinterpret_cast<uint4*>(&s_rcodes[r * QT_RLD + 32 * b]);
+    d[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    d[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    s_rscales[2 * r + b] = (uint8_t)sc;
+    __syncthreads();
+    const size_t row0 = (size_t)te * Kd + p0;
+#pragma unroll
+    for (int i = threadIdx.x; i < MX_KTILE * (QT_F / 16); i += 256) {
+      const int rr = i / (QT_F / 16), ch = i % (QT_F / 16);
+      *reinterpret_cast<uint4*>(row_codes + (row0 + rr) * F + f0 + 16 * ch) =
+          *reinterpret_cast<const uint4*>(&s_rcodes[rr * QT_RLD + 16 * ch]);
+    }
+    if (threadIdx.x < MX_KTILE)
+      *reinterpret_cast<uint16_t*>(row_scales + (row0 + threadIdx.x) * (F / 32) + f0 / 32) =
+          *reinterpret_cast<const uint16_t*>(&s_rscales[2 * threadIdx.x]);
+  }
 
   // one feature x one block of 32 rows per thread (a wave = 64 features of one
   // block); codes and scales are staged in LDS so that the stores run along
@@ -181,7 +225,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
   {
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = s_tile[(32 * q + i) * QT_LD + f];
+    for (int i = 0; i < 32; ++i) v[i] = ElemTraits<T>::load(&s_tile[(32 * q + i) * QT_LD + f]);
     uint32_t packed[8];
     const uint32_t sc = mx_quant_block(v, packed);
     uint4* d = reinterpret_cast<uint4*>(&s_codes[f * QT_CLD + 32 * q]);
@@ -216,10 +260,24 @@ template hipError_t launch_mx_quant_rows<bf16_t>(const bf16_t*, int, int, const 
 template hipError_t launch_mx_quant_rows<float>(const float*, int, int, const int32_t*, int, uint8_t*, uint8_t*,
                                                 hipStream_t);
 
+// blocks for nf x np x ne tiles, a multiple of the 8 XCDs
+inline int qt_grid(int F, int np, int ne) {
+  const long tiles = (long)((F + QT_F - 1) / QT_F) * np * ne;
+  return (int)((tiles + 7) / 8 * 8);
+}
+
 hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s) {
-  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false>), dim3((N + QT_F - 1) / QT_F, Kd / MX_KTILE, E), dim3(256),
-                     0, s, src, N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes, scales);
+  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s, src,
+                     N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes, scales, Kd / MX_KTILE, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_both(const bf16_t* src, int E, int Kd, int N, uint8_t* codes_t, uint8_t* scales_t,
+                                uint8_t* codes_r, uint8_t* scales_r, hipStream_t s) {
+  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false, true>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s,
+                     src, N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes_t, scales_t, Kd / MX_KTILE, E, codes_r,
+                     scales_r);
   return hipGetLastError();
 }
 
@@ -232,8 +290,8 @@ template <typename T>
 hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,
                                     const int32_t* pad_off, int E, int Mp, uint8_t* codes, uint8_t* scales,
                                     hipStream_t s) {
-  hipLaunchKernelGGL((mx_quant_t_kernel<T, true>), dim3((F + QT_F - 1) / QT_F, Mp / MX_KTILE), dim3(256), 0, s,
-                     src, F, s2f, k, offsets, pad_off, E, 0, Mp, codes, scales);
+  hipLaunchKernelGGL((mx_quant_t_kernel<T, true>), dim3(qt_grid(F, Mp / MX_KTILE, 1)), dim3(256), 0, s, src, F, s2f,
+                     k, offsets, pad_off, E, 0, Mp, codes, scales, Mp / MX_KTILE, 1);
   return hipGetLastError();
 }
 template hipError_t launch_mx_quant_tokens_t<bf16_t>(const bf16_t*, int, const int32_t*, int, const int32_t*,

@@ -108,14 +108,19 @@ moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routin
  *   G13[r] = x[t(r)] W13[e]^T,  A = SiLU(G1) * G3,  O = A W2[e]^T   (per expert e)
  *   y[t]   = sum_j gate[t,j] * O[flat_to_sorted[t*k+j]]               (fp32 sum in slot order)
  * x, w13, w2: device inputs; y: device output [T,H]; saved: device buffer of
- * the size reported (G13 of every routed row), to be passed unchanged to
- * moe_backward.
+ * the size reported (G13 of every routed row; in MOE_MODE_MXFP8 also the
+ * backward's weight codes), to be passed unchanged to moe_backward.
  *
  * MOE_MODE_MXFP8 (Prime Mega MoE news page, "How does the fused kernel
  * work?": BF16 and MXFP8 precisions): both GEMMs read their operands as
  * MXFP8 quantised along K as moe_mxfp8_quantize describes (x and W13 along H,
- * A and W2 along I; A is quantised from its fp32 value inside GEMM W13); SwiGLU, the combine
- * and y stay as above.  Its backward is the MOE_MODE_FP8_BWD backward. */
+ * A and W2 along I; A is quantised from its fp32 value inside GEMM W13);
+ * SwiGLU, the combine and y stay as above.  Its backward is the
+ * MOE_MODE_FP8_BWD backward.  Each weight is read once and quantised both
+ * ways: the forward's row-wise copy, and the transposed copy of the backward
+ * (W13 along 2I, W2 along H), which goes into `saved`; in this mode
+ * moe_backward takes its weight operands from `saved` and reads w13/w2 only
+ * through it, so the weights must not change between the two calls. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                        const moe_routing* routing, void* y, void* saved,
                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -160,11 +165,15 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  *             SwiGLU + quantise A, quantise W2, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
  *             unpermute-reduce, router backward, wgrad W2, wgrad W13
- *   backward, MOE_MODE_FP8_BWD and MOE_MODE_MXFP8: tile table, padded
- *             expert offsets, quantise W2^T, quantise dy, dgrad W2 + SwiGLU
- *             derivative + quantise dG13 and gate*A, quantise W13^T, dgrad
- *             W13, unpermute-reduce, router backward, quantise dy^T, wgrad
- *             W2, quantise x^T, wgrad W13 */
+ *   backward, MOE_MODE_FP8_BWD: tile table, padded expert offsets,
+ *             quantise W2^T, quantise dy, dgrad W2 + SwiGLU derivative +
+ *             quantise dG13 and gate*A, quantise W13^T, dgrad W13,
+ *             unpermute-reduce, router backward, quantise dy^T, wgrad W2,
+ *             quantise x^T, wgrad W13
+ *   backward, MOE_MODE_MXFP8: the same without quantise W2^T and quantise
+ *             W13^T (their codes come from `saved`)
+ *   forward, MOE_MODE_MXFP8, "quantise W13" / "quantise W2" write both
+ *             copies of the weight */
 moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                              const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events, int n_events);

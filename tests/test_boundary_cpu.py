@@ -181,10 +181,11 @@ class _NullStream:
 def test_mxfp8_mode_dims_and_kernel_counts():
     g, lib = _lib()
     ok = g.Dims.of(64, 128, 128, 8, 2, "mxfp8")
-    assert g.num_kernels(ok, "forward") == 7 and g.num_kernels(ok, "backward") == 13
+    assert g.num_kernels(ok, "forward") == 7 and g.num_kernels(ok, "backward") == 11
     rws, saved, fws, bws = g.workspace_size(ok)
     M = 64 * 2
-    assert saved >= M * 2 * 128 * 4                       # G13 kept in fp32
+    # G13 kept in fp32, plus the transposed weight codes the backward reuses
+    assert saved >= M * 2 * 128 * 4 + 8 * 3 * 128 * 128 * 33 // 32
     assert fws >= 64 * 128 + 8 * 3 * 128 * 128 + M * 128   # MXFP8 copies of x, W13, W2, A (A never stored unquantised)
     sz = ctypes.c_size_t(0)
     bad = g.Dims.of(64, 128, 64, 8, 2, "mxfp8")            # I must be a multiple of 128
