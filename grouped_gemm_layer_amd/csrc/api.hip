@@ -24,7 +24,7 @@ struct Sizes {
   size_t r_partials, r_bases;
   size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
   size_t f_qx, f_sx, f_qw13, f_sw13, f_qa, f_sa, f_qw2, f_sw2;   // mxfp8 forward operands
-  size_t b_tile_e, b_tile_r, b_tile_x, b_dG13, b_Ag, b_dXp, b_part;
+  size_t b_tile_e, b_tile_r, b_tile_x, b_wg_order, b_dG13, b_Ag, b_dXp, b_part;
   // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
   size_t Mp;
   // mxfp8: the transposed weight operands of the backward, kept in `saved` by the forward
@@ -97,6 +97,7 @@ Sizes compute_sizes(const moe_dims* d) {
   s.b_tile_e = o; o += align_up(max_tiles_b * 4);
   s.b_tile_r = o; o += align_up(max_tiles_b * 4);
   s.b_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
+  s.b_wg_order = o; o += align_up((size_t)d->E * 4);
   if (!mx8_backward(d->mode)) {   // the MXFP8 backward quantises them in the dgrad epilogue instead
     s.b_dG13 = o; o += align_up(M * 2 * d->I * es);
     s.b_Ag = o;   o += align_up(M * d->I * es);
@@ -272,7 +273,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     if (e == hipSuccess) e = r;
     if (e == hipSuccess) e = mk.mark();
   };
-  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream));
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, nullptr, stream));
   if (mx8_forward(dims->mode)) {
     auto u8 = [&](size_t off) { return reinterpret_cast<uint8_t*>(at(ws, off)); };
     Mx8Args q{};
@@ -334,7 +335,8 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.b_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.b_tile_r));
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
-  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
+  int32_t* wgo = reinterpret_cast<int32_t*>(at(ws, s.b_wg_order));
+  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx; a.wg_order = wgo;
   const int bm = bwd_row_tile_m(dims->mode);
   const Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
@@ -345,7 +347,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     if (e == hipSuccess) e = r;
     if (e == hipSuccess) e = mk.mark();
   };
-  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, stream));
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, wgo, stream));
   if (mx8) {
     // the dgrad epilogue of W2 places its token blocks at the padded offsets
     if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, const_cast<int32_t*>(q.pad_off), stream));

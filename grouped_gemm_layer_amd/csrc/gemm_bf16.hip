@@ -139,12 +139,13 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---------------- tile decode (XCD-contiguous renumbering) ----------------
-  const int per_xcd = gridDim.x / NXCD;
-  const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-  if (L >= tiles_total) return;
+  // ---------------- tile decode (row kinds: XCD-contiguous renumbering of the
+  // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, klo = 0, khi = 0, nk;
   if constexpr (K_::ragged_rows) {
+    const int per_xcd = gridDim.x / NXCD;
+    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+    if (L >= tiles_total) return;
     gg::RowTile rt;
     if (!gg::decode_row_tile(a, L, n_tiles, C::GROUP, rt)) return;
     e = rt.e;
@@ -156,8 +157,8 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     nk = Kd / BK;
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
-    e = L / per_e;
-    const int t = L % per_e;
+    int t;
+    if (!decode_wgrad_tile(a.wg_order, a.E, per_e, e, t)) return;
     m0 = (t / n_tiles) * BM;
     n0 = (t % n_tiles) * BN;
     klo = a.offsets[e];
@@ -427,7 +428,8 @@ hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
     n_tiles = (ndim + C::BN - 1) / C::BN;
     tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
   }
-  const int grid = (tiles + NXCD - 1) / NXCD * NXCD;
+  const int grid = Kind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
+                                           : wgrad_grid(a.E, tiles / a.E);
   hipLaunchKernelGGL((gemm_bf16_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, n_tiles, tiles);
   return hipGetLastError();
 }

@@ -96,12 +96,13 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---------------- tile decode (XCD-contiguous renumbering) ----------------
-  const int per_xcd = gridDim.x / NXCD;
-  const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-  if (L >= tiles_total) return;
+  // ---------------- tile decode (row kinds: XCD-contiguous renumbering of the
+  // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, nk, kp0 = 0;
   if constexpr (MxKind<KIND>::ragged_rows) {
+    const int per_xcd = gridDim.x / NXCD;
+    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+    if (L >= tiles_total) return;
     gg::RowTile rt;
     if (!gg::decode_row_tile(a, L, n_tiles, C::GROUP, rt)) return;
     e = rt.e;
@@ -111,8 +112,8 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     nk = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 ? H : KIND == KIND_FWD2 ? I : 2 * I) / KT;
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
-    e = L / per_e;
-    const int t = L % per_e;
+    int t;
+    if (!decode_wgrad_tile(a.wg_order, a.E, per_e, e, t)) return;
     m0 = (t / n_tiles) * BM;
     n0 = (t % n_tiles) * BN;
     kp0 = q.pad_off[e];
@@ -301,7 +302,8 @@ hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
     n_tiles = (ndim + C::BN - 1) / C::BN;
     tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
   }
-  const int grid = (tiles + NXCD - 1) / NXCD * NXCD;
+  const int grid = MxKind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
+                                             : wgrad_grid(a.E, tiles / a.E);
   hipLaunchKernelGGL((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles);
   return hipGetLastError();
 }

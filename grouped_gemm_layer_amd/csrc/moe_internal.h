@@ -61,6 +61,7 @@ struct LayerArgs {
   const int32_t* tile_expert;     // [max_tiles]
   const int32_t* tile_row0;       // [max_tiles]
   const int32_t* expert_tile0;    // [E+1] first row tile of each expert
+  const int32_t* wg_order;        // [E] experts by decreasing row count (weight-gradient tile order)
   // inputs
   const void* x;                  // [T,H]
   const void* w13;                // [E,2I,H]
@@ -134,7 +135,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 int route_num_blocks(int M);   // blocks of the histogram / scatter passes
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles,
-                             int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, hipStream_t s);
+                             int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, int32_t* wg_order, hipStream_t s);
 
 // combine / unpermute-reduce (fp32 accumulate in slot order)
 template <typename T>
@@ -186,6 +187,21 @@ constexpr int FP32_BN = 64;
 // mode: 0 fp32, 1 bf16, 2 mxfp8, 3 fp8_bwd (the public moe_mode values)
 inline bool mx8_forward(int mode) { return mode == 2; }
 inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
+// Weight-gradient tile t of the grid: block b goes to XCD b % 8 (round-robin
+// dispatch); XCD x takes the experts of rank x, x + 8, x + 16, ... in
+// decreasing row count, each as per_e consecutive tiles (which share the
+// expert's rows in that XCD's L2), so the longest tiles start first and the
+// largest experts spread over the XCDs.  Returns false past the last expert.
+__device__ __forceinline__ bool decode_wgrad_tile(const int32_t* wg_order, int E, int per_e, int& e, int& t) {
+  const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+  const int rank = x + 8 * (j / per_e);
+  if (rank >= E) return false;
+  e = wg_order[rank];
+  t = j % per_e;
+  return true;
+}
+inline int wgrad_grid(int E, int per_e) { return 8 * ((E + 7) / 8) * per_e; }
+
 inline int fwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
 }

@@ -187,15 +187,23 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 // Tile table of the row-ragged GEMMs: tile i covers rows [row0, row0 + bm) of
 // expert tile_expert[i] (clipped to the expert's end); unused tiles get -1.
 // expert_tile0[e] = first tile of expert e (expert_tile0[E] = number of tiles).
+// wg_order (optional): the experts by decreasing row count, ties by index --
+// the order in which the weight-gradient GEMMs take them, so that the longest
+// tiles start first (longest-processing-time-first list scheduling).
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                           int max_tiles, int32_t* __restrict__ tile_expert,
                                                           int32_t* __restrict__ tile_row0,
-                                                          int32_t* __restrict__ expert_tile0) {
+                                                          int32_t* __restrict__ expert_tile0,
+                                                          int32_t* __restrict__ wg_order) {
   __shared__ int s_start[2][MAX_E + 1];
+  __shared__ int s_cnt[MAX_E];
   const int e = threadIdx.x;
   int cur = 0;
   int nt = 0;
-  if (e < E) nt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  if (e < E) {
+    s_cnt[e] = offsets[e + 1] - offsets[e];
+    nt = (s_cnt[e] + bm - 1) / bm;
+  }
   if (e <= MAX_E) s_start[0][e] = (e < E) ? nt : 0;
   __syncthreads();
   for (int off = 1; off <= MAX_E; off <<= 1) {
@@ -206,6 +214,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     }
     cur ^= 1;
     __syncthreads();
+  }
+  if (wg_order && e < E) {   // rank of e by (count desc, index asc); s_cnt is visible after the scan's barriers
+    const int c = s_cnt[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (s_cnt[f] > c) || (s_cnt[f] == c && f < e);
+    wg_order[rank] = e;
   }
   // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
   const int total = s_start[cur][E - 1];
@@ -228,9 +242,9 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 }
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles, int32_t* tile_expert,
-                             int32_t* tile_row0, int32_t* expert_tile0, hipStream_t s) {
+                             int32_t* tile_row0, int32_t* expert_tile0, int32_t* wg_order, hipStream_t s) {
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
-                     tile_row0, expert_tile0);
+                     tile_row0, expert_tile0, wg_order);
   return hipGetLastError();
 }
 

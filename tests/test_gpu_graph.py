@@ -21,6 +21,7 @@ def _outputs(L):
 @pytest.mark.parametrize("dims,seed", [
     (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True), 401),
     (mi.LayerDims(T=300, H=256, I=128, E=8, k=2, dtype="bf16", mode="fp8_bwd"), 402),
+    (mi.LayerDims(T=500, H=256, I=128, E=8, k=4, dtype="bf16", skew=True, mode="mxfp8"), 403),
 ])
 def test_graph_replays_match_eager(dims, seed):
     import torch
