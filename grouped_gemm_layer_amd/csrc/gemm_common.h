@@ -230,7 +230,9 @@ __device__ __forceinline__ void staged_store(void* smem, Val&& val, T* out, size
 //   m = m0 + wm*WM + 16 i + lane%16,  n = n0 + wn*WN + 16 j + 4*(lane/16) + v
 // (for the SwiGLU kind the first FN/2 column blocks are G1 and the rest the
 // matching G3 columns).  `smem` is the kernel's operand LDS, free by now.
-template <int KIND, class C, bool F32IO = false>
+// MX8: epilogue of the MXFP8 kernels -- GEMM W13 + SwiGLU writes A as the
+// MXFP8 operand of GEMM W2 (the dgrad of W2 has dgrad2_epilogue_mx8).
+template <int KIND, class C, bool MX8 = false>
 __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)[C::FM][C::FN], void* smem,
                                               int tid, int lane, int wm, int wn, int e, int m0, int mlim,
                                               int n0, int nlim) {
@@ -262,7 +264,7 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       staged_store<C, FH>(smem, [&](int i, int j) { return gv(i, j + FH); }, G13 + I, ld13, m0, mlim, c0, I, tid,
                           lane, wm, wn);
     }
-    if constexpr (F32IO) {
+    if constexpr (MX8) {
       // MXFP8 operand of the GEMM W2 straight from fp32: blocks of 32 along I
       // are fragment pairs (2jb, 2jb+1); the 4 lanes sharing a row reduce the
       // block maximum with row swaps, codes leave through LDS along rows and
@@ -296,7 +298,7 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
     staged_store<C, FN>(smem, [&](int i, int j) { const f32x4_t v = acc[i][j]; return pack4(v[0], v[1], v[2], v[3]); },
                         out, (size_t)H, m0, mlim, n0, nlim, tid, lane, wm, wn);
   } else if constexpr (KIND == KIND_DGRAD2) {
-    static_assert(!F32IO, "the MXFP8 modes use dgrad2_epilogue_mx8");
+    static_assert(!MX8, "the MXFP8 kernels use dgrad2_epilogue_mx8");
     // dA' = acc passes through LDS in fp32, CH rows at a time; then each
     // thread takes 8 consecutive columns of one row: coalesced 16-byte loads
     // of G1 and G3, stores of dG1, dG3 and g*A, and the row's gate-gradient

@@ -68,7 +68,7 @@ struct LayerArgs {
   const void* w2;                 // [E,H,I]
   const void* dy;                 // [T,H]
   // forward intermediates / outputs
-  int g13_f32;                    // G13 stored in fp32 (fp8_bwd mode) instead of the activation type
+  int g13_f32;                    // G13 stored in fp32 (the MXFP8 backward) instead of the activation type
   void* G13;                      // [M,2I]  (saved)
   void* A;                        // [M,I]
   uint8_t* q_a;                   // mxfp8 mode: MXFP8 codes of A [M,I] (written by the GEMM W13 epilogue)
@@ -162,7 +162,7 @@ int mx8_dgrad2_tile_n();    // columns per tile of the MXFP8 dgrad of W2
 //   tokens_t:  src rows r of the expert-sorted order (gathered as above) of a
 //              [.][F] matrix -> codes [F][Mp], scales [F][Mp/32], expert e's
 //              rows at pad_off[e] .. (zero-padded to the next multiple of MX_KTILE)
-template <typename T>   // T = bf16_t or float
+template <typename T>   // instantiated for T = bf16_t
 hipError_t launch_mx_quant_rows(const T* src, int R, int K, const int32_t* s2f, int k, uint8_t* codes,
                                 uint8_t* scales, hipStream_t s);
 hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
@@ -174,7 +174,7 @@ hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8
 hipError_t launch_mx_quant_both(const bf16_t* src, int E, int Kd, int N, uint8_t* codes_t, uint8_t* scales_t,
                                 uint8_t* codes_r, uint8_t* scales_r, hipStream_t s);
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t s);
-template <typename T>   // T = bf16_t or float
+template <typename T>   // instantiated for T = bf16_t
 hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,
                                     const int32_t* pad_off, int E, int Mp, uint8_t* codes, uint8_t* scales,
                                     hipStream_t s);

@@ -257,8 +257,6 @@ hipError_t launch_mx_quant_rows(const T* src, int R, int K, const int32_t* s2f, 
 }
 template hipError_t launch_mx_quant_rows<bf16_t>(const bf16_t*, int, int, const int32_t*, int, uint8_t*, uint8_t*,
                                                  hipStream_t);
-template hipError_t launch_mx_quant_rows<float>(const float*, int, int, const int32_t*, int, uint8_t*, uint8_t*,
-                                                hipStream_t);
 
 // blocks for nf x np x ne tiles, a multiple of the 8 XCDs
 inline int qt_grid(int F, int np, int ne) {
@@ -296,7 +294,5 @@ hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int
 }
 template hipError_t launch_mx_quant_tokens_t<bf16_t>(const bf16_t*, int, const int32_t*, int, const int32_t*,
                                                      const int32_t*, int, int, uint8_t*, uint8_t*, hipStream_t);
-template hipError_t launch_mx_quant_tokens_t<float>(const float*, int, const int32_t*, int, const int32_t*,
-                                                    const int32_t*, int, int, uint8_t*, uint8_t*, hipStream_t);
 
 }  // namespace moe
