@@ -405,12 +405,21 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile).
+// Forward: 256 x 256 tiles with a 64-wide K tile (128-byte rows per DMA
+// lane group, one 8-wave block per CU): fewer operand bytes per flop and full
+// cache lines outweigh the longer ragged tail (measured 8 % faster for both
+// forward GEMMs).  The dgrad kinds measured faster with 128 x 256, K tile 32,
+// two 4-wave blocks per CU.
+#ifndef MOE_CFG_ROW_FWD
+#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64
+#endif
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
 #endif
 #ifndef MOE_CFG_WGRAD
 #define MOE_CFG_WGRAD 256, 256, 2, 4, 2, 2, 32
 #endif
+using CfgRowF = TileCfg<MOE_CFG_ROW_FWD>;
 using CfgRow = TileCfg<MOE_CFG_ROW>;
 using CfgW = TileCfg<MOE_CFG_WGRAD>;
 
@@ -436,13 +445,14 @@ hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int bf16_fwd_row_tile_m() { return CfgRowF::BM; }
 int bf16_row_tile_m() { return CfgRow::BM; }
 int bf16_dgrad2_tile_n() { return CfgRow::BN; }
 
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s) {
   switch (kind) {
-    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRow>(a, s);
-    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRow>(a, s);
+    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRowF>(a, s);
+    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRowF>(a, s);
     case KIND_DGRAD2: return launch_kind<KIND_DGRAD2, CfgRow>(a, s);
     case KIND_DGRAD1: return launch_kind<KIND_DGRAD1, CfgRow>(a, s);
     case KIND_WGRAD2: return launch_kind<KIND_WGRAD2, CfgW>(a, s);

@@ -180,7 +180,8 @@ hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int
                                     hipStream_t s);
 
 // tiling the API layer needs for workspace sizing and the tile table
-int bf16_row_tile_m();      // token rows per tile of the row-ragged bf16 GEMMs
+int bf16_fwd_row_tile_m();  // token rows per tile of the bf16 forward GEMMs
+int bf16_row_tile_m();      // token rows per tile of the bf16 dgrad GEMMs
 int bf16_dgrad2_tile_n();   // columns per tile of the bf16 dgrad of W2
 constexpr int FP32_BM = 64;
 constexpr int FP32_BN = 64;
@@ -203,7 +204,7 @@ __device__ __forceinline__ bool decode_wgrad_tile(const int32_t* wg_order, int E
 inline int wgrad_grid(int E, int per_e) { return 8 * ((E + 7) / 8) * per_e; }
 
 inline int fwd_row_tile_m(int mode) {
-  return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
+  return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_row_tile_m() : bf16_fwd_row_tile_m();
 }
 inline int bwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_backward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
