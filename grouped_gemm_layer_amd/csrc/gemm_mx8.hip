@@ -285,6 +285,10 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
 #ifndef MOE_MX8_CFG_WGRAD
 #define MOE_MX8_CFG_WGRAD 256, 256, 2, 4, 2, 2, 64
 #endif
+#ifndef MOE_MX8_CFG_ROW_FWD
+#define MOE_MX8_CFG_ROW_FWD 128, 128, 2, 2, 2, 2, 64
+#endif
+using CfgRowF = TileCfg<MOE_MX8_CFG_ROW_FWD>;   // forward kinds (their own tile table)
 using CfgRow = TileCfg<MOE_MX8_CFG_ROW>;
 using CfgW = TileCfg<MOE_MX8_CFG_WGRAD>;
 
@@ -310,13 +314,14 @@ hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
 
 }  // namespace
 
+int mx8_fwd_row_tile_m() { return CfgRowF::BM; }
 int mx8_row_tile_m() { return CfgRow::BM; }
 int mx8_dgrad2_tile_n() { return CfgRow::BN; }
 
 hipError_t launch_gemm_mx8(GemmKind kind, const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
   switch (kind) {
-    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRow>(a, q, s);
-    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRow>(a, q, s);
+    case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRowF>(a, q, s);
+    case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRowF>(a, q, s);
     case KIND_DGRAD2: return launch_kind<KIND_DGRAD2, CfgRow>(a, q, s);
     case KIND_DGRAD1: return launch_kind<KIND_DGRAD1, CfgRow>(a, q, s);
     case KIND_WGRAD2: return launch_kind<KIND_WGRAD2, CfgW>(a, q, s);

@@ -152,7 +152,8 @@ hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s);
 
 // MXFP8 GEMMs (every kind)
 hipError_t launch_gemm_mx8(GemmKind kind, const LayerArgs& a, const Mx8Args& q, hipStream_t s);
-int mx8_row_tile_m();       // token rows per tile of the row-ragged MXFP8 GEMMs
+int mx8_fwd_row_tile_m();   // token rows per tile of the MXFP8 forward GEMMs
+int mx8_row_tile_m();       // token rows per tile of the MXFP8 dgrad GEMMs
 int mx8_dgrad2_tile_n();    // columns per tile of the MXFP8 dgrad of W2
 
 // MXFP8 quantisers (E4M3FN codes + E8M0 scales per 32 elements, round to
@@ -204,7 +205,7 @@ __device__ __forceinline__ bool decode_wgrad_tile(const int32_t* wg_order, int E
 inline int wgrad_grid(int E, int per_e) { return 8 * ((E + 7) / 8) * per_e; }
 
 inline int fwd_row_tile_m(int mode) {
-  return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_row_tile_m() : bf16_fwd_row_tile_m();
+  return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_fwd_row_tile_m() : bf16_fwd_row_tile_m();
 }
 inline int bwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_backward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
