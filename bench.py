@@ -32,9 +32,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 FWD_KERNELS = ["tile_table", "gemm1_swiglu", "gemm2", "combine"]
 FWD_KERNELS_MX8 = ["tile_table", "quant_x", "quant_w13", "gemm1_swiglu", "quant_w2", "gemm2", "combine"]
-BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1"]
+BWD_KERNELS = ["tile_table_b", "dgrad2_dswiglu", "dgrad1", "unpermute_reduce", "router_bwd", "wgrad2", "wgrad1",
+               "wgrad_reduce"]
 BWD_KERNELS_FP8 = ["tile_table_b", "pad_offsets", "quant_w2t", "quant_dy", "dgrad2_dswiglu", "quant_w13t",
-                   "dgrad1", "unpermute_reduce", "router_bwd", "quant_dyt", "wgrad2", "quant_xt", "wgrad1"]
+                   "dgrad1", "unpermute_reduce", "router_bwd", "quant_dyt", "wgrad2", "quant_xt", "wgrad1",
+                   "wgrad_reduce"]
 # mxfp8 mode: the forward quantises each weight both ways, the backward reuses W2^T and W13^T codes
 BWD_KERNELS_MXFP8 = [n for n in BWD_KERNELS_FP8 if n not in ("quant_w2t", "quant_w13t")]
 

@@ -24,7 +24,8 @@ struct Sizes {
   size_t r_partials, r_bases;
   size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
   size_t f_qx, f_sx, f_qw13, f_sw13, f_qa, f_sa, f_qw2, f_sw2;   // mxfp8 forward operands
-  size_t b_tile_e, b_tile_r, b_tile_x, b_wg_order, b_dG13, b_Ag, b_dXp, b_part;
+  size_t b_tile_e, b_tile_r, b_tile_x, b_wg_order, b_wg_cstart, b_wg_slot0, b_wpart13, b_wpart2;
+  size_t b_dG13, b_Ag, b_dXp, b_part;
   // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
   size_t Mp;
   // mxfp8: the transposed weight operands of the backward, kept in `saved` by the forward
@@ -97,7 +98,14 @@ Sizes compute_sizes(const moe_dims* d) {
   s.b_tile_e = o; o += align_up(max_tiles_b * 4);
   s.b_tile_r = o; o += align_up(max_tiles_b * 4);
   s.b_tile_x = o; o += align_up(((size_t)d->E + 1) * 4);
-  s.b_wg_order = o; o += align_up((size_t)d->E * 4);
+  s.b_wg_order = o;  o += align_up((size_t)d->E * 4);
+  s.b_wg_cstart = o; o += align_up(((size_t)d->E + 1) * 4);
+  s.b_wg_slot0 = o;  o += align_up((size_t)d->E * 4);
+  if (d->mode != MOE_MODE_FP32) {   // fp32 partial results of the chunks c > 0 of split experts
+    const size_t slots = wgrad_max_slots(M);
+    s.b_wpart13 = o; o += align_up(slots * 2 * d->I * d->H * 4);
+    s.b_wpart2 = o;  o += align_up(slots * d->H * d->I * 4);
+  }
   if (!mx8_backward(d->mode)) {   // the MXFP8 backward quantises them in the dgrad epilogue instead
     s.b_dG13 = o; o += align_up(M * 2 * d->I * es);
     s.b_Ag = o;   o += align_up(M * d->I * es);
@@ -191,15 +199,19 @@ constexpr int kForwardKernels = 4;    // tile table, GEMM1+SwiGLU, GEMM2, combin
 // mxfp8: tile table, quant x, quant W13, GEMM1+SwiGLU+quant A, quant W2, GEMM2, combine
 constexpr int kForwardKernelsMx8 = 7;
 inline int forward_kernels(int mode) { return mx8_forward(mode) ? kForwardKernelsMx8 : kForwardKernels; }
-constexpr int kBackwardKernels = 7;   // tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13
+// tile table, dgrad W2 + dSwiGLU, dgrad W13, unpermute, router, wgrad W2, wgrad W13,
+// and (bf16) the ordered split-K completion of the weight gradients
+constexpr int kBackwardKernels = 7;
 // MXFP8 backward: tile table, padded offsets, quant W2^T, quant dY, dgrad W2 +
 // dSwiGLU + quant dG13 (row and token blocks) and gate*A (token blocks),
 // quant W13^T, dgrad W13, unpermute, router, quant dY^T, wgrad W2, quant x^T,
-// wgrad W13
-constexpr int kBackwardKernelsMx8 = 13;
+// wgrad W13, split-K completion
+constexpr int kBackwardKernelsMx8 = 14;
 // MOE_MODE_MXFP8: the same without the two weight quantisers (the forward saved W2^T and W13^T codes)
 inline int backward_kernels(int mode) {
-  return mx8_forward(mode) ? kBackwardKernelsMx8 - 2 : mx8_backward(mode) ? kBackwardKernelsMx8 : kBackwardKernels;
+  return mx8_forward(mode) ? kBackwardKernelsMx8 - 2
+         : mx8_backward(mode) ? kBackwardKernelsMx8
+         : mode == MOE_MODE_FP32 ? kBackwardKernels : kBackwardKernels + 1;
 }
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
@@ -273,7 +285,8 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     if (e == hipSuccess) e = r;
     if (e == hipSuccess) e = mk.mark();
   };
-  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, nullptr, stream));
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, WgradList{},
+                         stream));
   if (mx8_forward(dims->mode)) {
     auto u8 = [&](size_t off) { return reinterpret_cast<uint8_t*>(at(ws, off)); };
     Mx8Args q{};
@@ -335,8 +348,18 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.b_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.b_tile_r));
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
-  int32_t* wgo = reinterpret_cast<int32_t*>(at(ws, s.b_wg_order));
-  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx; a.wg_order = wgo;
+  a.tile_expert = te; a.tile_row0 = tr; a.expert_tile0 = tx;
+  // weight-gradient work list (bf16 and MXFP8 kernels; the fp32 kernels take whole experts)
+  const bool split = bf16;
+  WgradList wg{};
+  if (split) {
+    wg.order = reinterpret_cast<int32_t*>(at(ws, s.b_wg_order));
+    wg.cstart = reinterpret_cast<int32_t*>(at(ws, s.b_wg_cstart));
+    wg.slot0 = reinterpret_cast<int32_t*>(at(ws, s.b_wg_slot0));
+    a.wg_order = wg.order; a.wg_cstart = wg.cstart; a.wg_slot0 = wg.slot0;
+    a.wpart13 = reinterpret_cast<float*>(at(ws, s.b_wpart13));
+    a.wpart2 = reinterpret_cast<float*>(at(ws, s.b_wpart2));
+  }
   const int bm = bwd_row_tile_m(dims->mode);
   const Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
@@ -347,7 +370,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     if (e == hipSuccess) e = r;
     if (e == hipSuccess) e = mk.mark();
   };
-  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, wgo, stream));
+  step(launch_tile_table(routing->offsets, dims->E, bm, max_row_tiles(a.M, a.E, bm), te, tr, tx, wg, stream));
   if (mx8) {
     // the dgrad epilogue of W2 places its token blocks at the padded offsets
     if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, const_cast<int32_t*>(q.pad_off), stream));
@@ -389,6 +412,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     if (e == hipSuccess) step(gemm(bf16, KIND_WGRAD2, a, stream));
     if (e == hipSuccess) step(gemm(bf16, KIND_WGRAD1, a, stream));
   }
+  if (split && e == hipSuccess) step(launch_wgrad_reduce(a, stream));
   return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

@@ -125,4 +125,55 @@ hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t
   return hipGetLastError();
 }
 
+// Split-K completion of the weight gradients: for each expert whose rows were
+// split into chunks (its rank r has cstart[r+1] - cstart[r] > 1 chunks; they
+// are the first ranks, the work list being ordered by decreasing row count),
+// dW[e] = chunk 0's result (already in dW) + the partial slots of chunks
+// 1, 2, ... added in that order, elementwise in fp32 -- deterministic, no
+// atomics.  blockIdx.y = rank, blockIdx.z = matrix (0: dW13, 1: dW2).
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int32_t* __restrict__ order,
+                                                           const int32_t* __restrict__ cstart,
+                                                           const int32_t* __restrict__ slot0,
+                                                           float* __restrict__ dw13, const float* __restrict__ p13,
+                                                           size_t n13, float* __restrict__ dw2,
+                                                           const float* __restrict__ p2, size_t n2) {
+  const int r = blockIdx.y;
+  const int nch = cstart[r + 1] - cstart[r];
+  if (nch <= 1) return;
+  const bool w13 = blockIdx.z == 0;
+  const size_t n = w13 ? n13 : n2;
+  float* dw = (w13 ? dw13 : dw2) + (size_t)order[r] * n;
+  const float* p = (w13 ? p13 : p2) + (size_t)slot0[r] * n;
+  constexpr int U = 4;                     // 16-byte vectors per thread per pass
+  const size_t step = (size_t)gridDim.x * 256 * 4 * U;
+  for (size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i0 < n; i0 += step) {
+    f32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + (size_t)u * gridDim.x * 256 * 4;
+      v[u] = i < n ? *reinterpret_cast<const f32x4_t*>(dw + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c = 1; c < nch; ++c) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = i0 + (size_t)u * gridDim.x * 256 * 4;
+        if (i < n) v[u] += *reinterpret_cast<const f32x4_t*>(p + (size_t)(c - 1) * n + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + (size_t)u * gridDim.x * 256 * 4;
+      if (i < n) *reinterpret_cast<f32x4_t*>(dw + i) = v[u];
+    }
+  }
+}
+
+hipError_t launch_wgrad_reduce(const LayerArgs& a, hipStream_t s) {
+  const int ranks = max(1, min(a.E, (int)wgrad_max_slots((size_t)a.M)));   // split experts come first
+  const size_t n13 = (size_t)2 * a.I * a.H, n2 = (size_t)a.H * a.I;
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(512, ranks, 2), dim3(256), 0, s, a.wg_order, a.wg_cstart,
+                     a.wg_slot0, a.dw13, a.wpart13, n13, a.dw2, a.wpart2, n2);
+  return hipGetLastError();
+}
+
 }  // namespace moe

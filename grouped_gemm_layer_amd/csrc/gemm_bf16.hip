@@ -142,6 +142,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   // ---------------- tile decode (row kinds: XCD-contiguous renumbering of the
   // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, klo = 0, khi = 0, nk;
+  float* wout = nullptr;   // weight gradients: dW[e], or the chunk's partial slot
   if constexpr (K_::ragged_rows) {
     const int per_xcd = gridDim.x / NXCD;
     const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
@@ -157,13 +158,14 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     nk = Kd / BK;
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
-    int t;
-    if (!decode_wgrad_tile(a.wg_order, a.E, per_e, e, t)) return;
+    int t, r0, r1, slot;
+    if (!decode_wgrad_tile(a, per_e, e, r0, r1, slot, t)) return;
     m0 = (t / n_tiles) * BM;
     n0 = (t % n_tiles) * BN;
-    klo = a.offsets[e];
-    khi = a.offsets[e + 1];
+    klo = a.offsets[e] + r0;
+    khi = a.offsets[e] + r1;
     nk = (khi - klo + BK - 1) / BK;
+    wout = gg::wgrad_out<KIND>(a, e, slot);
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
   const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
@@ -401,7 +403,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
 
-  gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim);
+  gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout);
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile).
@@ -438,7 +440,7 @@ hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
     tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
   }
   const int grid = Kind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
-                                           : wgrad_grid(a.E, tiles / a.E);
+                                           : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
   hipLaunchKernelGGL((gemm_bf16_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, n_tiles, tiles);
   return hipGetLastError();
 }

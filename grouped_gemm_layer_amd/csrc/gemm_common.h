@@ -226,6 +226,15 @@ __device__ __forceinline__ void staged_store(void* smem, Val&& val, T* out, size
   __syncthreads();
 }
 
+// Output of a weight-gradient tile: dW[e] for the first chunk of expert e,
+// else the chunk's partial slot (added to dW[e] in chunk order afterwards).
+template <int KIND>
+__device__ __forceinline__ float* wgrad_out(const LayerArgs& a, int e, int slot) {
+  const size_t n = KIND == KIND_WGRAD2 ? (size_t)a.H * a.I : (size_t)2 * a.I * a.H;
+  float* base = slot < 0 ? (KIND == KIND_WGRAD2 ? a.dw2 : a.dw13) : (KIND == KIND_WGRAD2 ? a.wpart2 : a.wpart13);
+  return base + (size_t)(slot < 0 ? e : slot) * n;
+}
+
 // Epilogue of one output tile.  acc[i][j][v] holds C[m][n] for
 //   m = m0 + wm*WM + 16 i + lane%16,  n = n0 + wn*WN + 16 j + 4*(lane/16) + v
 // (for the SwiGLU kind the first FN/2 column blocks are G1 and the rest the
@@ -235,7 +244,7 @@ __device__ __forceinline__ void staged_store(void* smem, Val&& val, T* out, size
 template <int KIND, class C, bool MX8 = false>
 __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)[C::FM][C::FN], void* smem,
                                               int tid, int lane, int wm, int wn, int e, int m0, int mlim,
-                                              int n0, int nlim) {
+                                              int n0, int nlim, float* wout = nullptr) {
   constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   const int H = a.H, I = a.I;
   // ---------------- epilogues ----------------
@@ -383,7 +392,7 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
     float* s_out = reinterpret_cast<float*>(smem);
     constexpr int NQ = BN / 4;                             // 16-byte chunks per row
     auto out_off = [&](int row, int q) { return row * BN + ((q ^ (row % NQ)) << 2); };
-    float* out = (KIND == KIND_WGRAD2) ? a.dw2 + (size_t)e * H * I : a.dw13 + (size_t)e * 2 * I * H;
+    float* out = wout;   // dW[e] or a partial slot of a split expert
     const int ld = (KIND == KIND_WGRAD2) ? I : H;
 #pragma unroll
     for (int ch = 0; ch < BM / CH; ++ch) {

@@ -99,6 +99,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   // ---------------- tile decode (row kinds: XCD-contiguous renumbering of the
   // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, nk, kp0 = 0;
+  float* wout = nullptr;   // weight gradients: dW[e], or the chunk's partial slot
   if constexpr (MxKind<KIND>::ragged_rows) {
     const int per_xcd = gridDim.x / NXCD;
     const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
@@ -112,12 +113,13 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     nk = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 ? H : KIND == KIND_FWD2 ? I : 2 * I) / KT;
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
-    int t;
-    if (!decode_wgrad_tile(a.wg_order, a.E, per_e, e, t)) return;
+    int t, r0, r1, slot;
+    if (!decode_wgrad_tile(a, per_e, e, r0, r1, slot, t)) return;
     m0 = (t / n_tiles) * BM;
     n0 = (t % n_tiles) * BN;
-    kp0 = q.pad_off[e];
-    nk = (a.offsets[e + 1] - a.offsets[e] + KT - 1) / KT;
+    kp0 = q.pad_off[e] + r0;              // chunks start on K-tile boundaries of the padded rows
+    nk = (r1 - r0 + KT - 1) / KT;
+    wout = gg::wgrad_out<KIND>(a, e, slot);
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
   const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
@@ -274,7 +276,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   if constexpr (KIND == KIND_DGRAD2)
     gg::dgrad2_epilogue_mx8<C>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
   else
-    gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim);
+    gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout);
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).  The
@@ -307,7 +309,7 @@ hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
     tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
   }
   const int grid = MxKind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
-                                             : wgrad_grid(a.E, tiles / a.E);
+                                             : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
   hipLaunchKernelGGL((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles);
   return hipGetLastError();
 }

@@ -61,7 +61,12 @@ struct LayerArgs {
   const int32_t* tile_expert;     // [max_tiles]
   const int32_t* tile_row0;       // [max_tiles]
   const int32_t* expert_tile0;    // [E+1] first row tile of each expert
-  const int32_t* wg_order;        // [E] experts by decreasing row count (weight-gradient tile order)
+  // weight-gradient work list (see WgradList) and the partial slots of split experts
+  const int32_t* wg_order;        // [E]   expert of each rank (decreasing row count)
+  const int32_t* wg_cstart;       // [E+1] first chunk of each rank; wg_cstart[E] = chunks
+  const int32_t* wg_slot0;        // [E]   first partial slot of each rank
+  float* wpart13;                 // [slots, 2I, H] fp32 partial dW13 of chunks c > 0
+  float* wpart2;                  // [slots, H, I]  fp32 partial dW2
   // inputs
   const void* x;                  // [T,H]
   const void* w13;                // [E,2I,H]
@@ -134,8 +139,24 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
                         int32_t* ws_partials, int32_t* ws_bases, hipStream_t s);
 int route_num_blocks(int M);   // blocks of the histogram / scatter passes
 
+// Rows per weight-gradient chunk: an expert with more rows is split along K
+// (its rows) into chunks of WG_KC rows (a multiple of the 128-row MXFP8 K tile
+// and of every bf16 K tile), whose fp32 results are summed in chunk order.
+constexpr int WG_KC = 4096;
+struct WgradList {              // device tables written by the backward's tile-table kernel
+  int32_t* order;               // [E]   expert of each rank, by decreasing row count (ties: index)
+  int32_t* cstart;              // [E+1] first chunk of each rank (exclusive prefix of the chunk counts)
+  int32_t* slot0;               // [E]   first partial slot of each rank (prefix of chunks - 1)
+};
+// partial slots the split experts can need: sum over experts of (chunks - 1) <= M / WG_KC
+inline size_t wgrad_max_slots(size_t M) { return M / WG_KC; }
+// upper bound of the number of chunks: E + M / WG_KC
+inline int wgrad_max_chunks(int M, int E) { return E + M / WG_KC; }
+
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles,
-                             int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, int32_t* wg_order, hipStream_t s);
+                             int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, WgradList wg, hipStream_t s);
+// dW[e] += the partial slots of each split expert, in chunk order (both matrices)
+hipError_t launch_wgrad_reduce(const LayerArgs& a, hipStream_t s);
 
 // combine / unpermute-reduce (fp32 accumulate in slot order)
 template <typename T>
@@ -189,20 +210,36 @@ constexpr int FP32_BN = 64;
 // mode: 0 fp32, 1 bf16, 2 mxfp8, 3 fp8_bwd (the public moe_mode values)
 inline bool mx8_forward(int mode) { return mode == 2; }
 inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
-// Weight-gradient tile t of the grid: block b goes to XCD b % 8 (round-robin
-// dispatch); XCD x takes the experts of rank x, x + 8, x + 16, ... in
-// decreasing row count, each as per_e consecutive tiles (which share the
-// expert's rows in that XCD's L2), so the longest tiles start first and the
-// largest experts spread over the XCDs.  Returns false past the last expert.
-__device__ __forceinline__ bool decode_wgrad_tile(const int32_t* wg_order, int E, int per_e, int& e, int& t) {
+// Weight-gradient tile of this block: block b goes to XCD b % 8 (round-robin
+// dispatch); in round q the XCDs take chunks 8q .. 8q + 7 of the work list
+// (experts by decreasing row count, an expert's chunks consecutive), XCD x
+// chunk 8q + x in even rounds and 8q + 7 - x in odd ones (a snake, so that no
+// XCD always draws the longest chunk of a round), each as per_e consecutive
+// tiles (which share the chunk's rows in that XCD's L2): the longest tiles
+// start first and the load of the XCDs stays even.
+// Gives the expert e, its rows [r0, r1) (expert-local), the partial slot (-1
+// for chunk 0, which writes dW[e]) and the tile t; false past the last chunk.
+__device__ __forceinline__ bool decode_wgrad_tile(const LayerArgs& a, int per_e, int& e, int& r0, int& r1,
+                                                  int& slot, int& t) {
   const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
-  const int rank = x + 8 * (j / per_e);
-  if (rank >= E) return false;
-  e = wg_order[rank];
+  const int q = j / per_e;
+  const int item = 8 * q + ((q & 1) ? 7 - x : x);
+  if (item >= a.wg_cstart[a.E]) return false;
+  int lo = 0, hi = a.E - 1;               // rank with cstart[rank] <= item (cstart strictly increasing)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.wg_cstart[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  e = a.wg_order[lo];
+  const int c = item - a.wg_cstart[lo];
+  const int cnt = a.offsets[e + 1] - a.offsets[e];
+  r0 = c * WG_KC;
+  r1 = min(cnt, r0 + WG_KC);
+  slot = c == 0 ? -1 : a.wg_slot0[lo] + c - 1;
   t = j % per_e;
   return true;
 }
-inline int wgrad_grid(int E, int per_e) { return 8 * ((E + 7) / 8) * per_e; }
+inline int wgrad_grid(int max_chunks, int per_e) { return 8 * ((max_chunks + 7) / 8) * per_e; }
 
 inline int fwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_fwd_row_tile_m() : bf16_fwd_row_tile_m();

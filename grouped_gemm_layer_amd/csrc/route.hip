@@ -187,14 +187,15 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 // Tile table of the row-ragged GEMMs: tile i covers rows [row0, row0 + bm) of
 // expert tile_expert[i] (clipped to the expert's end); unused tiles get -1.
 // expert_tile0[e] = first tile of expert e (expert_tile0[E] = number of tiles).
-// wg_order (optional): the experts by decreasing row count, ties by index --
-// the order in which the weight-gradient GEMMs take them, so that the longest
-// tiles start first (longest-processing-time-first list scheduling).
+// Weight-gradient work list (optional, `wg` non-null; see WgradList): the
+// experts by decreasing row count, ties by index (longest-processing-time-
+// first list scheduling), each split into chunks of at most WG_KC rows (an
+// empty expert is one empty chunk); chunk c > 0 of an expert accumulates into
+// a partial slot that the ordered reduction adds to chunk 0's result.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                           int max_tiles, int32_t* __restrict__ tile_expert,
                                                           int32_t* __restrict__ tile_row0,
-                                                          int32_t* __restrict__ expert_tile0,
-                                                          int32_t* __restrict__ wg_order) {
+                                                          int32_t* __restrict__ expert_tile0, WgradList wg) {
   __shared__ int s_start[2][MAX_E + 1];
   __shared__ int s_cnt[MAX_E];
   const int e = threadIdx.x;
@@ -215,11 +216,26 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     cur ^= 1;
     __syncthreads();
   }
-  if (wg_order && e < E) {   // rank of e by (count desc, index asc); s_cnt is visible after the scan's barriers
-    const int c = s_cnt[e];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (s_cnt[f] > c) || (s_cnt[f] == c && f < e);
-    wg_order[rank] = e;
+  if (wg.order) {
+    __shared__ int s_nch[MAX_E];            // chunks of the expert of each rank
+    if (e < E) {   // rank of e by (count desc, index asc); s_cnt is visible after the scan's barriers
+      const int c = s_cnt[e];
+      int rank = 0;
+      for (int f = 0; f < E; ++f) rank += (s_cnt[f] > c) || (s_cnt[f] == c && f < e);
+      wg.order[rank] = e;
+      s_nch[rank] = c > WG_KC ? (c + WG_KC - 1) / WG_KC : 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {                 // E <= 512: a serial prefix over the ranks
+      int cs = 0, sl = 0;
+      for (int r = 0; r < E; ++r) {
+        wg.cstart[r] = cs;
+        wg.slot0[r] = sl;
+        cs += s_nch[r];
+        sl += s_nch[r] - 1;
+      }
+      wg.cstart[E] = cs;
+    }
   }
   // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
   const int total = s_start[cur][E - 1];
@@ -242,9 +258,9 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 }
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles, int32_t* tile_expert,
-                             int32_t* tile_row0, int32_t* expert_tile0, int32_t* wg_order, hipStream_t s) {
+                             int32_t* tile_row0, int32_t* expert_tile0, WgradList wg, hipStream_t s) {
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
-                     tile_row0, expert_tile0, wg_order);
+                     tile_row0, expert_tile0, wg);
   return hipGetLastError();
 }
 

@@ -133,6 +133,8 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, con
  *   dx[t] = sum_j (dG13 W13[e])[row of slot j]       (fp32 sum in slot order)
  *   dw2[e]  = sum_r dy[t(r)]^T (gate_r A_r)          (fp32 accumulate and output)
  *   dw13[e] = sum_r dG13_r^T x[t(r)]                 (fp32; zero for an empty expert)
+ *     (an expert with more than 4096 rows sums these over chunks of 4096 rows,
+ *     each accumulated in fp32, then added in chunk order: deterministic)
  *   dlogits[t,e] = gate_e (dgate_e - sum_j gate_j dgate_j) on the top-k set, else 0
  * dy, x, w13, w2: device inputs; saved: from moe_forward; dx: device [T,H];
  * dw13, dw2: device fp32, overwritten; dgate: device [T,k] fp32; dlogits:
@@ -164,12 +166,14 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
  *   forward, MOE_MODE_MXFP8: tile table, quantise x, quantise W13, GEMM W13 +
  *             SwiGLU + quantise A, quantise W2, GEMM W2, combine
  *   backward: tile table, dgrad W2 + SwiGLU derivative, dgrad W13,
- *             unpermute-reduce, router backward, wgrad W2, wgrad W13
+ *             unpermute-reduce, router backward, wgrad W2, wgrad W13, and
+ *             (all modes but MOE_MODE_FP32) the split-K completion of the
+ *             weight gradients
  *   backward, MOE_MODE_FP8_BWD: tile table, padded expert offsets,
  *             quantise W2^T, quantise dy, dgrad W2 + SwiGLU derivative +
  *             quantise dG13 and gate*A, quantise W13^T, dgrad W13,
  *             unpermute-reduce, router backward, quantise dy^T, wgrad W2,
- *             quantise x^T, wgrad W13
+ *             quantise x^T, wgrad W13, split-K completion
  *   backward, MOE_MODE_MXFP8: the same without quantise W2^T and quantise
  *             W13^T (their codes come from `saved`)
  *   forward, MOE_MODE_MXFP8, "quantise W13" / "quantise W2" write both

@@ -134,8 +134,8 @@ def test_num_kernels_by_mode():
     bf = g.Dims.of(64, 128, 64, 8, 2, "bf16")
     f8 = g.Dims.of(64, 128, 64, 8, 2, "fp8_bwd")
     assert g.num_kernels(bf, "route") == 4 and g.num_kernels(bf, "forward") == 4
-    assert g.num_kernels(bf, "backward") == 7
-    assert g.num_kernels(f8, "forward") == 4 and g.num_kernels(f8, "backward") == 13
+    assert g.num_kernels(bf, "backward") == 8
+    assert g.num_kernels(f8, "forward") == 4 and g.num_kernels(f8, "backward") == 14
     assert lib.moe_num_kernels(ctypes.byref(g.Dims.of(0, 128, 64, 8, 2, "bf16")), 1) == -1
     assert lib.moe_num_kernels(ctypes.byref(bf), 7) == -1
 
@@ -181,7 +181,7 @@ class _NullStream:
 def test_mxfp8_mode_dims_and_kernel_counts():
     g, lib = _lib()
     ok = g.Dims.of(64, 128, 128, 8, 2, "mxfp8")
-    assert g.num_kernels(ok, "forward") == 7 and g.num_kernels(ok, "backward") == 11
+    assert g.num_kernels(ok, "forward") == 7 and g.num_kernels(ok, "backward") == 12
     rws, saved, fws, bws = g.workspace_size(ok)
     M = 64 * 2
     # G13 kept in fp32, plus the transposed weight codes the backward reuses

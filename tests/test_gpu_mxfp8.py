@@ -176,6 +176,18 @@ def test_fp8_bwd_one_expert_takes_all():
     assert run.routing_np()["counts"].tolist() == [0, 0, 0, 0, 0, 300, 0, 0]
 
 
+def test_fp8_bwd_split_heavy_expert():
+    """MXFP8 weight gradients of experts split into several 4096-row chunks
+    (chunk boundaries fall on 128-row K tiles of the padded token operands)."""
+    d = mi.LayerDims(T=9000, H=256, I=64, E=4, k=2, dtype="bf16", mode="fp8_bwd")
+    inp = mi.make_inputs(d, 306)
+    inp["logits"][:, 0] += 4.0            # moderate biases: no gate underflows
+    inp["logits"][: d.T // 2, 1] += 2.0
+    run = _compare_fp8_bwd(d, inp)
+    c = run.routing_np()["counts"]
+    assert c[0] > 2 * 4096 and c[1] > 4096
+
+
 def test_fp8_bwd_fullsize_sampled():
     """The Qwen3-30B-A3B shape with the MXFP8 backward, in the launch
     configuration the benchmark times; sampled outputs against both oracles."""

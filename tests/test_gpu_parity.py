@@ -78,6 +78,20 @@ def test_edge_all_tokens_to_one_expert():
     assert run.routing_np()["counts"].tolist() == [0, 0, 0, 400, 0, 0, 0, 0]
 
 
+def test_wgrad_split_heavy_expert():
+    """Experts with more rows than one weight-gradient chunk (4096 rows): their
+    dW13 and dW2 are summed from several chunks in chunk order.  Expert 0
+    takes every token (9000 rows: three chunks), expert 1 at least half of
+    them (two chunks), the rest a few hundred each."""
+    d = mi.LayerDims(T=9000, H=128, I=64, E=4, k=2, dtype="bf16")
+    inp = mi.make_inputs(d, 111)
+    inp["logits"][:, 0] += 4.0            # moderate biases: no gate underflows
+    inp["logits"][: d.T // 2, 1] += 2.0
+    run, _ = _full_compare(d, inp, TOL["bf16"])
+    c = run.routing_np()["counts"]
+    assert c[0] > 2 * 4096 and c[1] > 4096
+
+
 def test_edge_single_token():
     d = mi.LayerDims(T=1, H=64, I=64, E=4, k=2, dtype="bf16")
     _full_compare(d, mi.make_inputs(d, 108), TOL["bf16"])
