@@ -85,6 +85,8 @@ def load_library():
                                  vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_workspace_size", "moe_route", "moe_forward", "moe_backward"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.moe_backward_accumulate.argtypes = lib.moe_backward.argtypes
+    lib.moe_backward_accumulate.restype = ctypes.c_int
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [vp, ctypes.c_int]
     lib.moe_backward_timed.argtypes = lib.moe_backward.argtypes + [vp, ctypes.c_int]
     lib.moe_forward_timed.restype = ctypes.c_int
@@ -177,13 +179,18 @@ def forward(dims: Dims, x, w13, w2, routing: RoutingBuffers, y, saved, ws, strea
 
 
 def backward(dims: Dims, dy, x, w13, w2, routing: RoutingBuffers, saved, dx, dw13, dw2, dgate, dlogits, ws,
-             stream=None, events=None):
-    """events: optional ctypes array of hipEvent_t (moe_backward_timed)."""
+             stream=None, events=None, accumulate=False):
+    """events: optional ctypes array of hipEvent_t (moe_backward_timed).
+    accumulate: add the weight gradients to dw13 / dw2 (moe_backward_accumulate)."""
     lib = load_library()
     r = routing.c()
     args = [ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(w13), _ptr(w2), ctypes.byref(r), _ptr(saved), _ptr(dx),
             _ptr(dw13), _ptr(dw2), _ptr(dgate), _ptr(dlogits), _ptr(ws), ws.numel(), _stream(stream)]
-    if events is None:
+    if accumulate:
+        if events is not None:
+            raise ValueError("timed accumulate-into is not provided")
+        _check(lib.moe_backward_accumulate(*args), "moe_backward_accumulate")
+    elif events is None:
         _check(lib.moe_backward(*args), "moe_backward")
     else:
         _check(lib.moe_backward_timed(*args, events, len(events)), "moe_backward_timed")
@@ -249,7 +256,7 @@ class MoeLayer:
         forward(self.dims, x, w13, w2, self.routing, self.y, self.saved, self.fwd_ws, stream, events)
         return self.y
 
-    def backward(self, dy, x, w13, w2, want_dlogits=True, stream=None, events=None):
+    def backward(self, dy, x, w13, w2, want_dlogits=True, stream=None, events=None, accumulate=False):
         backward(self.dims, dy, x, w13, w2, self.routing, self.saved, self.dx, self.dw13, self.dw2, self.dgate,
-                 self.dlogits if want_dlogits else None, self.bwd_ws, stream, events)
+                 self.dlogits if want_dlogits else None, self.bwd_ws, stream, events, accumulate)
         return self.dx, self.dw13, self.dw2, self.dgate, (self.dlogits if want_dlogits else None)

@@ -219,7 +219,8 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
                         hipStream_t stream, Marks mk);
 moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,
                          const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
-                         float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk);
+                         float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk,
+                         bool accumulate = false);
 
 }  // namespace
 
@@ -324,7 +325,8 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
 
 moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,
                          const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
-                         float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk) {
+                         float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk,
+                         bool accumulate) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_routing(routing)) != MOE_OK) return st;
@@ -345,6 +347,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   a.dgate_part = reinterpret_cast<float*>(at(ws, s.b_part));
   a.dw13 = dw13;
   a.dw2 = dw2;
+  a.wgrad_acc = accumulate ? 1 : 0;
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.b_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.b_tile_r));
   int32_t* tx = reinterpret_cast<int32_t*>(at(ws, s.b_tile_x));
@@ -445,6 +448,14 @@ moe_status moe_forward_timed(const moe_dims* dims, const void* x, const void* w1
   if (check_dims(dims) == MOE_OK && n_events < forward_kernels(dims->mode) + 1) return MOE_ERR_DIMS;
   return forward_impl(dims, x, w13, w2, routing, y, saved, ws, ws_bytes, stream,
                       Marks{events, n_events, 0, stream});
+}
+
+moe_status moe_backward_accumulate(const moe_dims* dims, const void* dy, const void* x, const void* w13,
+                                   const void* w2, const moe_routing* routing, const void* saved, void* dx,
+                                   float* dw13, float* dw2, float* dgate, float* dlogits, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return backward_impl(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws, ws_bytes, stream,
+                       Marks{nullptr, 0, 0, stream}, true);
 }
 
 moe_status moe_backward_timed(const moe_dims* dims, const void* dy, const void* x, const void* w13,

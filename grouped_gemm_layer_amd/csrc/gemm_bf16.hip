@@ -143,6 +143,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, klo = 0, khi = 0, nk;
   float* wout = nullptr;   // weight gradients: dW[e], or the chunk's partial slot
+  bool wacc = false;       //   dW[e] adds the caller's value (accumulate-into)
   if constexpr (K_::ragged_rows) {
     const int per_xcd = gridDim.x / NXCD;
     const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
@@ -166,6 +167,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     khi = a.offsets[e] + r1;
     nk = (khi - klo + BK - 1) / BK;
     wout = gg::wgrad_out<KIND>(a, e, slot);
+    wacc = a.wgrad_acc && slot < 0;
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
   const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
@@ -403,7 +405,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
 
-  gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout);
+  gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout, wacc);
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile).

@@ -228,6 +228,7 @@ __device__ __forceinline__ void staged_store(void* smem, Val&& val, T* out, size
 
 // Output of a weight-gradient tile: dW[e] for the first chunk of expert e,
 // else the chunk's partial slot (added to dW[e] in chunk order afterwards).
+// With accumulate-into (a.wgrad_acc) only dW[e] adds the caller's value.
 template <int KIND>
 __device__ __forceinline__ float* wgrad_out(const LayerArgs& a, int e, int slot) {
   const size_t n = KIND == KIND_WGRAD2 ? (size_t)a.H * a.I : (size_t)2 * a.I * a.H;
@@ -244,7 +245,7 @@ __device__ __forceinline__ float* wgrad_out(const LayerArgs& a, int e, int slot)
 template <int KIND, class C, bool MX8 = false>
 __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)[C::FM][C::FN], void* smem,
                                               int tid, int lane, int wm, int wn, int e, int m0, int mlim,
-                                              int n0, int nlim, float* wout = nullptr) {
+                                              int n0, int nlim, float* wout = nullptr, bool wacc = false) {
   constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   const int H = a.H, I = a.I;
   // ---------------- epilogues ----------------
@@ -411,8 +412,11 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       for (int c = tid; c < CH * NQ; c += NTHR) {
         const int row = c / NQ, q = c % NQ;
         const int m = m0 + ch * CH + row, n = n0 + 4 * q;
-        if (m < mlim && n < nlim)
-          st_out<true>(out + (size_t)m * ld + n, *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
+        if (m < mlim && n < nlim) {
+          f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]);
+          if (wacc) v = *reinterpret_cast<const f32x4_t*>(out + (size_t)m * ld + n) + v;   // accumulate-into
+          st_out<true>(out + (size_t)m * ld + n, v);
+        }
       }
     }
   }

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void gemm_fp32_kernel(LayerArgs a, int n_tiles
     for (int i = tid; i < BM * BN; i += 256) {
       const int mm = i / BN, nn = i % BN;
       const int m = m0 + mm, n = n0 + nn;
-      if (m < mlim && n < nlim) out[(size_t)m * ld + n] = sC[mm][nn];
+      if (m < mlim && n < nlim) out[(size_t)m * ld + n] = a.wgrad_acc ? out[(size_t)m * ld + n] + sC[mm][nn] : sC[mm][nn];
     }
   }
 }

@@ -100,6 +100,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, nk, kp0 = 0;
   float* wout = nullptr;   // weight gradients: dW[e], or the chunk's partial slot
+  bool wacc = false;       //   dW[e] adds the caller's value (accumulate-into)
   if constexpr (MxKind<KIND>::ragged_rows) {
     const int per_xcd = gridDim.x / NXCD;
     const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
@@ -120,6 +121,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     kp0 = q.pad_off[e] + r0;              // chunks start on K-tile boundaries of the padded rows
     nk = (r1 - r0 + KT - 1) / KT;
     wout = gg::wgrad_out<KIND>(a, e, slot);
+    wacc = a.wgrad_acc && slot < 0;
     mlim = (KIND == KIND_WGRAD2) ? H : 2 * I;
   }
   const int nlim = (KIND == KIND_FWD1 || KIND == KIND_DGRAD2 || KIND == KIND_WGRAD2) ? I : H;
@@ -276,7 +278,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   if constexpr (KIND == KIND_DGRAD2)
     gg::dgrad2_epilogue_mx8<C>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
   else
-    gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout);
+    gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout, wacc);
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).  The

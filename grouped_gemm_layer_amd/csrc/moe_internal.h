@@ -85,6 +85,7 @@ struct LayerArgs {
   void* dXp;                      // [M,H]
   float* dgate_part;              // [n_parts, M]
   float* dw13;                    // [E,2I,H]
+  int wgrad_acc;                  // weight gradients are added to dw13 / dw2 (accumulate-into)
   float* dw2;                     // [E,H,I]
 };
 

@@ -156,6 +156,19 @@ moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, con
                         void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_backward, except that the weight gradients are added to what dw13 and
+ * dw2 hold (an fp32 main-gradient buffer accumulated over micro-batches):
+ * dw[e] = ((dw_in[e] + chunk 0) + chunk 1) + ... in fp32, deterministic; an
+ * empty expert leaves its entries unchanged.  All other outputs as in
+ * moe_backward.  dw13, dw2: device fp32, read and written.  For training
+ * loops that keep fp32 gradients across micro-batches (the weight gradients
+ * are the backward's independent half: neurobober digest, "Overlapping
+ * Backward Pass"). */
+moe_status moe_backward_accumulate(const moe_dims* dims, const void* dy, const void* x, const void* w13,
+                                   const void* w2, const moe_routing* routing, const void* saved,
+                                   void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Benchmarking variants of moe_forward / moe_backward: the same work, and in
  * addition events[0] is recorded on `stream` before the first kernel and
  * events[i+1] after kernel i, so that hipEventElapsedTime(events[i],

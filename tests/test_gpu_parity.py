@@ -92,6 +92,48 @@ def test_wgrad_split_heavy_expert():
     assert c[0] > 2 * 4096 and c[1] > 4096
 
 
+@pytest.mark.parametrize("dims,seed", [
+    (mi.LayerDims(T=300, H=128, I=64, E=8, k=2, dtype="fp32"), 112),
+    (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True), 113),
+    (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True, mode="fp8_bwd"), 114),
+    (mi.LayerDims(T=9000, H=128, I=64, E=4, k=2, dtype="bf16"), 115),   # split experts
+])
+def test_backward_accumulate_into(dims, seed):
+    """moe_backward_accumulate adds the weight gradients to what dw13 / dw2
+    hold: against the plain backward's result G and a random start R, an
+    expert in one chunk gives R + G exactly (one fp32 add per element; empty
+    experts keep R), a split expert (R + chunk 0) + chunk 1 ... within fp32
+    rounding; every other output is bitwise that of the plain backward."""
+    import torch
+    inp = mi.make_inputs(dims, seed)
+    if dims.T == 9000:
+        inp["logits"][:, 0] += 4.0
+        inp["logits"][: dims.T // 2, 1] += 2.0
+    print(f"[accumulate] dims={dims}", flush=True)
+    run = GpuRun(dims, inp)
+    run.run_all()
+    L = run.layer
+    G13, G2 = L.dw13.clone(), L.dw2.clone()
+    others = [t.clone() for t in (L.dx, L.dgate, L.dlogits)]
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    R13 = torch.randn(G13.shape, device="cuda", generator=gen)
+    R2 = torch.randn(G2.shape, device="cuda", generator=gen)
+    L.dw13.copy_(R13)
+    L.dw2.copy_(R2)
+    run.layer.backward(run.dy, run.x, run.w13, run.w2, accumulate=True)
+    torch.cuda.synchronize()
+    for a, b in zip((L.dx, L.dgate, L.dlogits), others):
+        assert torch.equal(a, b)
+    counts = run.routing_np()["counts"]
+    for got, R, G in ((L.dw13, R13, G13), (L.dw2, R2, G2)):
+        for e in range(dims.E):
+            if counts[e] <= 4096:
+                assert torch.equal(got[e], R[e] + G[e]), e
+            else:
+                err = (got[e] - (R[e] + G[e])).abs().max().item()
+                assert err <= 1e-5 * (R[e].abs().max().item() + G[e].abs().max().item()), (e, err)
+
+
 def test_edge_single_token():
     d = mi.LayerDims(T=1, H=64, I=64, E=4, k=2, dtype="bf16")
     _full_compare(d, mi.make_inputs(d, 108), TOL["bf16"])
