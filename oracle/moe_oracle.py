@@ -50,6 +50,10 @@ The pages print no formula.  The readings taken where they are silent:
       operands quantised along their K (x and W13 along H, A and W2 along I);
       SwiGLU and the combine stay in full precision; the backward is the
       fp8_bwd backward applied to this forward's state.
+  R13 router projection (TE dropless-MoE page, "01 Why is MoE training
+      harder than dense training?": the router is a trained component, so it
+      has a gradient): logits = x W_r^T with W_r [E, H], no bias; its backward
+      adds dlogits W_r to dx and gives dW_r = dlogits^T x.
 
 Every function below is pinned by tests/test_oracle_*.py against something
 other than itself (finite differences, closed forms, brute force, the
@@ -222,6 +226,19 @@ def router_backward(gate: np.ndarray, dgate: np.ndarray, idx: np.ndarray, E: int
     dL = np.zeros((T, E))
     np.put_along_axis(dL, np.asarray(idx, dtype=np.int64), dsel, axis=1)
     return dL
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """Router projection (R13): logits[t, e] = <x[t], W_r[e]>."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+
+
+def router_projection_backward(dlogits: np.ndarray, x: np.ndarray, w_router: np.ndarray) -> dict:
+    """Backward of logits = x W_r^T (R13): the router's share of dx and the
+    router weight gradient."""
+    dl = np.asarray(dlogits, dtype=np.float64)
+    return {"dx": dl @ np.asarray(w_router, dtype=np.float64),
+            "dw_router": dl.T @ np.asarray(x, dtype=np.float64)}
 
 
 def backward(dy, x, w13, w2, r: Routing, state: dict, *, want_dw=True):

@@ -195,3 +195,50 @@ def test_golden_expert_example():
     assert np.allclose(Y, gd["y"], rtol=1e-14, atol=0)
     for key in ("dx", "dw13", "dw2", "dgate"):
         assert np.allclose(g[key], gd[key], rtol=1e-14, atol=1e-15), key
+
+
+def test_router_projection_finite_differences():
+    """Router projection (R13): L(x, W_r) = <dY, layer(x, route(x W_r^T))>.
+    Central differences in x (which reaches the loss through the experts and
+    through the logits) and in W_r pin dx = dx_experts + dlogits W_r and
+    dW_r = dlogits^T x."""
+    d = mi.CONFIGS[1]
+    inp = {kk: v.astype(np.float64) for kk, v in mi.make_inputs(d, 1).items()}
+    rng = np.random.default_rng(5)
+    wr = rng.standard_normal((d.E, d.H)) * 0.1
+    dy = inp["dy"]
+
+    def loss(x, w):
+        rr = orc.route(orc.router_logits(x, w), d.k)
+        Yp, _ = orc.forward(x, inp["w13"], inp["w2"], rr)
+        return float(np.sum(dy * Yp))
+
+    logits = orc.router_logits(inp["x"], wr)
+    r = orc.route(logits, d.k)
+    _, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    g = orc.backward(dy, inp["x"], inp["w13"], inp["w2"], r, st)
+    pr = orc.router_projection_backward(g["dlogits"], inp["x"], wr)
+    dx = g["dx"] + pr["dx"]
+    # the projection's own pieces against the definition of a matrix product
+    assert np.allclose(logits, np.einsum("th,eh->te", inp["x"], wr), rtol=0, atol=1e-12)
+    h = 1e-6
+    margin = np.sort(logits, axis=1)[:, ::-1]
+    margin = margin[:, d.k - 1] - margin[:, d.k]
+    checks = 0
+    for name, arr, an_full in (("x", inp["x"], dx), ("w", wr, pr["dw_router"])):
+        for _ in range(8):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            toks = [pos[0]] if name == "x" else range(d.T)
+            # a perturbation must not change any token's top-k set
+            if min(margin[t] for t in toks) < 1e3 * h * (np.abs(wr).max() + np.abs(inp["x"]).max()):
+                continue
+            p = arr.copy(); p[pos] += h
+            m = arr.copy(); m[pos] -= h
+            fd = (loss(p, wr) - loss(m, wr)) / (2 * h) if name == "x" else \
+                (loss(inp["x"], p) - loss(inp["x"], m)) / (2 * h)
+            an = an_full[pos]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, pos, fd, an)
+            checks += 1
+    assert checks >= 10
+    # the router's share of dx is not negligible here (the pin would miss a dropped term)
+    assert np.abs(pr["dx"]).max() > 1e-3 * np.abs(g["dx"]).max()
