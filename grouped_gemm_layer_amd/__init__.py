@@ -85,6 +85,10 @@ def load_library():
                                  vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_workspace_size", "moe_route", "moe_forward", "moe_backward"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.moe_route_project.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, ctypes.POINTER(_CRouting), vp, sz, vp]
+    lib.moe_route_project.restype = ctypes.c_int
+    lib.moe_router_backward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_CRouting), vp, vp, vp, vp, vp, vp]
+    lib.moe_router_backward.restype = ctypes.c_int
     lib.moe_backward_accumulate.argtypes = lib.moe_backward.argtypes
     lib.moe_backward_accumulate.restype = ctypes.c_int
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [vp, ctypes.c_int]
@@ -164,6 +168,22 @@ def route(dims: Dims, logits, routing: RoutingBuffers, ws, stream=None):
     r = routing.c()
     _check(lib.moe_route(ctypes.byref(dims), _ptr(logits), ctypes.byref(r), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_route")
+
+
+def route_project(dims: Dims, x, w_router, logits, routing: RoutingBuffers, ws, stream=None):
+    """logits = x w_router^T (written to `logits`), then route (moe_route_project)."""
+    lib = load_library()
+    r = routing.c()
+    _check(lib.moe_route_project(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), ctypes.byref(r),
+                                 _ptr(ws), ws.numel(), _stream(stream)), "moe_route_project")
+
+
+def router_backward(dims: Dims, routing: RoutingBuffers, dlogits, x, w_router, dx, dw_router, stream=None):
+    """dx += dlogits w_router; dw_router = dlogits^T x (moe_router_backward)."""
+    lib = load_library()
+    r = routing.c()
+    _check(lib.moe_router_backward(ctypes.byref(dims), ctypes.byref(r), _ptr(dlogits), _ptr(x), _ptr(w_router),
+                                   _ptr(dx), _ptr(dw_router), _stream(stream)), "moe_router_backward")
 
 
 def forward(dims: Dims, x, w13, w2, routing: RoutingBuffers, y, saved, ws, stream=None, events=None):
@@ -251,6 +271,18 @@ class MoeLayer:
 
     def route(self, logits, stream=None):
         route(self.dims, logits, self.routing, self.route_ws, stream)
+
+    def route_project(self, x, w_router, stream=None):
+        """Router projection logits = x w_router^T (kept in self.logits), then route."""
+        import torch
+        if getattr(self, "logits", None) is None:
+            self.logits = torch.empty((self.dims.T, self.dims.E), dtype=torch.float32, device=self.device)
+        route_project(self.dims, x, w_router, self.logits, self.routing, self.route_ws, stream)
+        return self.logits
+
+    def router_backward(self, x, w_router, dw_router, stream=None):
+        """After backward(want_dlogits=True): dx += dlogits w_router, dw_router = dlogits^T x."""
+        router_backward(self.dims, self.routing, self.dlogits, x, w_router, self.dx, dw_router, stream)
 
     def forward(self, x, w13, w2, stream=None, events=None):
         forward(self.dims, x, w13, w2, self.routing, self.y, self.saved, self.fwd_ws, stream, events)

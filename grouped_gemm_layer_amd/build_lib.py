@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_gfx950.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "combine.hip", "gemm_bf16.hip", "gemm_fp32.hip", "mxfp8.hip", "gemm_mx8.hip", "api.hip"]
+SOURCES = ["route.hip", "router.hip", "combine.hip", "gemm_bf16.hip", "gemm_fp32.hip", "mxfp8.hip", "gemm_mx8.hip", "api.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -254,6 +254,42 @@ moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routin
   return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+moe_status moe_route_project(const moe_dims* dims, const void* x, const void* w_router, float* logits,
+                             const moe_routing* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->mode == MOE_MODE_FP32) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_routing(out)) != MOE_OK) return st;
+  if (!x || !w_router || !logits || !ws) return MOE_ERR_NULL;
+  if (!aligned(x) || !aligned(w_router) || !aligned(logits) || !aligned(ws)) return MOE_ERR_ALIGN;
+  const Sizes s = compute_sizes(dims);
+  if (ws_bytes < s.route_ws) return MOE_ERR_WORKSPACE;
+  hipError_t e = launch_router_logits(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router), dims->T,
+                                      dims->H, dims->E, logits, stream);
+  if (e == hipSuccess)
+    e = launch_route(logits, dims->T, dims->E, dims->k, out->topk_idx, out->gate, out->counts, out->offsets,
+                     out->sorted_to_flat, out->flat_to_sorted, reinterpret_cast<int32_t*>(at(ws, s.r_partials)),
+                     reinterpret_cast<int32_t*>(at(ws, s.r_bases)), stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status moe_router_backward(const moe_dims* dims, const moe_routing* routing, const float* dlogits,
+                               const void* x, const void* w_router, void* dx, float* dw_router,
+                               hipStream_t stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->mode == MOE_MODE_FP32) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_routing(routing)) != MOE_OK) return st;
+  if (!dlogits || !x || !w_router || !dx || !dw_router) return MOE_ERR_NULL;
+  if (!aligned(dlogits) || !aligned(x) || !aligned(w_router) || !aligned(dx) || !aligned(dw_router))
+    return MOE_ERR_ALIGN;
+  const hipError_t e = launch_router_project_bwd(
+      dlogits, routing->topk_idx, routing->offsets, routing->sorted_to_flat, static_cast<const bf16_t*>(x),
+      static_cast<const bf16_t*>(w_router), dims->T, dims->H, dims->E, dims->k, static_cast<bf16_t*>(dx), dw_router,
+      stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 }  // extern "C"
 
 namespace {

@@ -135,6 +135,12 @@ enum GemmKind {
 // Launchers (each returns hipGetLastError() of its launch).
 // ---------------------------------------------------------------------------
 // routing
+// router projection (router.hip): logits = x W_r^T; backward: dx += dlogits W_r, dW_r = dlogits^T x
+hipError_t launch_router_logits(const bf16_t* x, const bf16_t* wr, int T, int H, int E, float* logits,
+                                hipStream_t s);
+hipError_t launch_router_project_bwd(const float* dlogits, const int32_t* topk_idx, const int32_t* offsets,
+                                     const int32_t* s2f, const bf16_t* x, const bf16_t* wr, int T, int H, int E,
+                                     int k, bf16_t* dx, float* dwr, hipStream_t s);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* gate,
                         int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
                         int32_t* ws_partials, int32_t* ws_bases, hipStream_t s);

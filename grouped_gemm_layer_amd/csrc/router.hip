@@ -1,0 +1,165 @@
+// Router projection and its backward (TE dropless-MoE page, "01 Why is MoE
+// training harder than dense training?": the router is trained, so it needs
+// a gradient; its form is the plain linear one, logits = x W_r^T):
+//   forward : logits[t, e] = <x[t], W_r[e]>                       (fp32)
+//   backward: dx[t]  += sum_j dlogits[t, idx[t,j]] W_r[idx[t,j]]   (dlogits is
+//             zero off the token's top-k set, so these k rows are the whole
+//             product dlogits W_r)
+//             dW_r[e] = sum over the rows r of expert e (ascending sorted
+//             order) of dlogits[t(r), e] x[t(r)]                   (fp32)
+// x and W_r are bf16.  Everything is deterministic (fixed summation orders,
+// no atomics).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// One wave per 64 tokens x 64 experts, K = H in steps of 32, operands read
+// straight from global memory into MFMA fragments (the projection is 2 T E H
+// flop, a few percent of the layer; its operands stay in L2).  With
+// v_mfma_f32_16x16x32_bf16 called as mfma(P, Q, c), lane l holds
+// sum_k P[4 (l/16) + v][k] Q[l%16][k], v = 0..3, and an operand fragment is
+// row l%16, K elements 8 (l/16) .. +7: here P = W_r rows (experts) and Q = x
+// rows (tokens), so a lane ends with 4 consecutive experts of one token.
+constexpr int RL_T = 64, RL_E = 64;
+
+__global__ __launch_bounds__(64) void router_logits_kernel(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ wr, int T, int H, int E,
+                                                           float* __restrict__ logits) {
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * RL_T, e0 = blockIdx.y * RL_E;
+  const int r = lane & 15, kq = 8 * (lane >> 4);
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // rows past T or E read row 0 (in bounds) and are never stored
+  const bf16_t* xr[4];
+  const bf16_t* wrr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * i + r, e = e0 + 16 * i + r;
+    xr[i] = x + (size_t)(t < T ? t : 0) * H + kq;
+    wrr[i] = wr + (size_t)(e < E ? e : 0) * H + kq;
+  }
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    bf16x8_t xf[4], wf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[i] = *reinterpret_cast<const bf16x8_t*>(xr[i] + k0);
+      wf[i] = *reinterpret_cast<const bf16x8_t*>(wrr[i] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)       // token block
+#pragma unroll
+      for (int j = 0; j < 4; ++j)     // expert block
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * i + r;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 16 * j + 4 * (lane >> 4);
+      float* dst = logits + (size_t)t * E + e;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (e + v < E) dst[v] = acc[i][j][v];
+    }
+  }
+}
+
+// dx[t] += sum_j dlogits[t, idx[t, j]] * W_r[idx[t, j]], fp32 in slot order
+// on top of dx's value, rounded once.  One block per token, 8 columns per
+// thread.
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dlogits,
+                                                        const int32_t* __restrict__ idx,
+                                                        const bf16_t* __restrict__ wr, int k, int H, int E,
+                                                        bf16_t* __restrict__ dx) {
+  __shared__ int s_e[32];
+  __shared__ float s_d[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    const int e = idx[(size_t)t * k + threadIdx.x];
+    s_e[threadIdx.x] = e;
+    s_d[threadIdx.x] = dlogits[(size_t)t * E + e];
+  }
+  __syncthreads();
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+    const uint4 d0 = *reinterpret_cast<const uint4*>(dx + (size_t)t * H + h0);
+    const uint32_t dw[4] = {d0.x, d0.y, d0.z, d0.w};
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = __uint_as_float(dw[i] << 16);
+      acc[2 * i + 1] = __uint_as_float(dw[i] & 0xFFFF0000u);
+    }
+    for (int j = 0; j < k; ++j) {
+      const uint4 w = *reinterpret_cast<const uint4*>(wr + (size_t)s_e[j] * H + h0);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      const float g = s_d[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += g * __uint_as_float(ww[i] << 16);
+        acc[2 * i + 1] += g * __uint_as_float(ww[i] & 0xFFFF0000u);
+      }
+    }
+    *reinterpret_cast<uint4*>(dx + (size_t)t * H + h0) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                   pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
+// dW_r[e][h] for one expert e (blockIdx.y) and 64 columns (one wave, one
+// column per lane): the expert's sorted rows in ascending order, 8 rows in
+// flight, fp32.  An expert with no rows writes zeros.
+__global__ __launch_bounds__(64) void router_dw_kernel(const float* __restrict__ dlogits,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ s2f, const bf16_t* __restrict__ x,
+                                                       int k, int H, int E, float* __restrict__ dwr) {
+  const int e = blockIdx.y;
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float acc = 0.f;
+  int r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    float xv[8], dv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int f = s2f[r + u];
+      const int t = f / k;
+      xv[u] = bf16_to_f32(x[(size_t)t * H + h]);
+      dv[u] = dlogits[(size_t)t * E + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += dv[u] * xv[u];
+  }
+  for (; r < r1; ++r) {
+    const int t = s2f[r] / k;
+    acc += dlogits[(size_t)t * E + e] * bf16_to_f32(x[(size_t)t * H + h]);
+  }
+  dwr[(size_t)e * H + h] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const bf16_t* x, const bf16_t* wr, int T, int H, int E, float* logits,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(router_logits_kernel, dim3((T + RL_T - 1) / RL_T, (E + RL_E - 1) / RL_E), dim3(64), 0, s, x,
+                     wr, T, H, E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_project_bwd(const float* dlogits, const int32_t* topk_idx, const int32_t* offsets,
+                                     const int32_t* s2f, const bf16_t* x, const bf16_t* wr, int T, int H, int E,
+                                     int k, bf16_t* dx, float* dwr, hipStream_t s) {
+  hipLaunchKernelGGL(router_dx_kernel, dim3(T), dim3(256), 0, s, dlogits, topk_idx, wr, k, H, E, dx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(router_dw_kernel, dim3(H / 64, E), dim3(64), 0, s, dlogits, offsets, s2f, x, k, H, E, dwr);
+  return hipGetLastError();
+}
+
+}  // namespace moe

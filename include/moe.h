@@ -104,6 +104,30 @@ moe_status moe_workspace_size(const moe_dims* dims, size_t* route_ws, size_t* sa
 moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Router projection, then moe_route (TE dropless-MoE page, "01 Why is MoE
+ * training harder than dense training?": the router is a trained component):
+ *   logits[t,e] = <x[t], w_router[e]>   (bf16 inputs, fp32 accumulation)
+ * x: device [T,H] bf16; w_router: device [E,H] bf16; logits: device [T,E]
+ * fp32, written (the top-k and gates are taken from these values exactly as
+ * moe_route takes its input).  Modes with bf16 activations only
+ * (MOE_ERR_UNSUPPORTED in MOE_MODE_FP32).  ws as for moe_route. */
+moe_status moe_route_project(const moe_dims* dims, const void* x, const void* w_router, float* logits,
+                             const moe_routing* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the router projection, after moe_backward produced dlogits and
+ * dx:
+ *   dx[t]      += sum_j dlogits[t, idx_j] w_router[idx_j]   (fp32 on top of
+ *                 dx's bf16 value, rounded once; dlogits is zero off the
+ *                 top-k set, so this is dlogits w_router)
+ *   dw_router[e] = sum over the rows r of expert e, in sorted order, of
+ *                 dlogits[t(r), e] x[t(r)]                   (fp32, written)
+ * dlogits: device [T,E] fp32 (moe_backward's); x, w_router as for
+ * moe_route_project; dx: device [T,H] bf16, read and written; dw_router:
+ * device [E,H] fp32.  No workspace.  MOE_ERR_UNSUPPORTED in MOE_MODE_FP32. */
+moe_status moe_router_backward(const moe_dims* dims, const moe_routing* routing, const float* dlogits,
+                               const void* x, const void* w_router, void* dx, float* dw_router,
+                               hipStream_t stream);
+
 /* Forward pass (Prime Mega MoE news page, "How does the fused kernel work?").
  *   G13[r] = x[t(r)] W13[e]^T,  A = SiLU(G1) * G3,  O = A W2[e]^T   (per expert e)
  *   y[t]   = sum_j gate[t,j] * O[flat_to_sorted[t*k+j]]               (fp32 sum in slot order)
