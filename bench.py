@@ -115,6 +115,33 @@ def recorded_traffic(config: int, kernel: str):
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def time_router_projection(g, layer, d, x, seed, K, W):
+    """moe_route_project (logits GEMM + routing) and moe_router_backward on
+    the layer's shape, after the timed steps (not part of a step)."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed + 1000)
+    wr = torch.from_numpy(rng.standard_normal((d.E, d.H)).astype(np.float32) * 0.05).to("cuda", torch.bfloat16)
+    dwr = torch.empty((d.E, d.H), dtype=torch.float32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for _ in range(W):
+        layer.route_project(x, wr)
+        layer.router_backward(x, wr, dwr)
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record()
+        layer.route_project(x, wr)
+        ev[i][1].record()
+        layer.router_backward(x, wr, dwr)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    return {"project_and_route_ms": round(fwd, 4), "backward_ms": round(bwd, 4),
+            "logits_flop": 2 * d.T * d.E * d.H,
+            "note": "logits = x W_r^T + routing; backward: dx += dlogits W_r, dW_r = dlogits^T x"}
+
+
 def copy_calibration(mib: int):
     """One plain device-to-device copy of `mib` MiB (bytes known exactly), for
     scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
@@ -282,6 +309,8 @@ def main():
         "gemm_mfma_frac": round(sum(flops[n] / (peak[n] * 1e12) for n in flops) / (gemm_ms * 1e-3), 4),
         "kernels": kernels, "roofline": roofline, "cpu_baseline": None,
     }
+    if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
+        out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_tokens)

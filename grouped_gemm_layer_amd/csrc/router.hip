@@ -5,8 +5,8 @@
 //   backward: dx[t]  += sum_j dlogits[t, idx[t,j]] W_r[idx[t,j]]   (dlogits is
 //             zero off the token's top-k set, so these k rows are the whole
 //             product dlogits W_r)
-//             dW_r[e] = sum over the rows r of expert e (ascending sorted
-//             order) of dlogits[t(r), e] x[t(r)]                   (fp32)
+//             dW_r[e] = sum over the rows r of expert e (in a fixed order
+//             over its sorted rows) of dlogits[t(r), e] x[t(r)]    (fp32)
 // x and W_r are bf16.  Everything is deterministic (fixed summation orders,
 // no atomics).
 #include "moe_internal.h"
@@ -112,35 +112,66 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
   }
 }
 
-// dW_r[e][h] for one expert e (blockIdx.y) and 64 columns (one wave, one
-// column per lane): the expert's sorted rows in ascending order, 8 rows in
-// flight, fp32.  An expert with no rows writes zeros.
-__global__ __launch_bounds__(64) void router_dw_kernel(const float* __restrict__ dlogits,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ s2f, const bf16_t* __restrict__ x,
-                                                       int k, int H, int E, float* __restrict__ dwr) {
+// dW_r[e][h] for one expert e (blockIdx.y) and 512 columns (8 per lane):
+// wave w of the block sums rows w, w + 4, w + 8, ... of the expert's sorted
+// rows (4 rows in flight), then the four partial sums are added in wave
+// order through LDS: fixed order, fp32.  An expert with no rows writes zeros.
+constexpr int RDW_COLS = 512;
+
+__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dlogits,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ s2f,
+                                                        const bf16_t* __restrict__ x, int k, int H, int E,
+                                                        float* __restrict__ dwr) {
+  __shared__ __attribute__((aligned(16))) float s_part[3][RDW_COLS];
   const int e = blockIdx.y;
-  const int h = blockIdx.x * 64 + threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h0 = blockIdx.x * RDW_COLS + 8 * lane;
+  const bool live = h0 < H;
   const int r0 = offsets[e], r1 = offsets[e + 1];
-  float acc = 0.f;
-  int r = r0;
-  for (; r + 8 <= r1; r += 8) {
-    float xv[8], dv[8];
+  float acc[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = s2f[r + u];
-      const int t = f / k;
-      xv[u] = bf16_to_f32(x[(size_t)t * H + h]);
-      dv[u] = dlogits[(size_t)t * E + e];
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  auto add_row = [&](uint4 v, float d) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += d * __uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += d * __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  };
+  int r = r0 + wave;
+  for (; r + 12 < r1; r += 16) {   // rows r, r+4, r+8, r+12 of this wave
+    uint4 v[4];
+    float d[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = s2f[r + 4 * u] / k;
+      d[u] = dlogits[(size_t)t * E + e];
+      v[u] = live ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += dv[u] * xv[u];
+    for (int u = 0; u < 4; ++u) add_row(v[u], d[u]);
   }
-  for (; r < r1; ++r) {
+  for (; r < r1; r += 4) {
     const int t = s2f[r] / k;
-    acc += dlogits[(size_t)t * E + e] * bf16_to_f32(x[(size_t)t * H + h]);
+    add_row(live ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0) : make_uint4(0u, 0u, 0u, 0u),
+            dlogits[(size_t)t * E + e]);
   }
-  dwr[(size_t)e * H + h] = acc;
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_part[wave - 1][8 * lane + i] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && live) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += s_part[w][8 * lane + i];
+    float* dst = dwr + (size_t)e * H + h0;
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+  }
 }
 
 }  // namespace
@@ -158,7 +189,8 @@ hipError_t launch_router_project_bwd(const float* dlogits, const int32_t* topk_i
   hipLaunchKernelGGL(router_dx_kernel, dim3(T), dim3(256), 0, s, dlogits, topk_idx, wr, k, H, E, dx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_dw_kernel, dim3(H / 64, E), dim3(64), 0, s, dlogits, offsets, s2f, x, k, H, E, dwr);
+  hipLaunchKernelGGL(router_dw_kernel, dim3((H + RDW_COLS - 1) / RDW_COLS, E), dim3(256), 0, s, dlogits, offsets,
+                     s2f, x, k, H, E, dwr);
   return hipGetLastError();
 }
 

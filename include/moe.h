@@ -119,7 +119,7 @@ moe_status moe_route_project(const moe_dims* dims, const void* x, const void* w_
  *   dx[t]      += sum_j dlogits[t, idx_j] w_router[idx_j]   (fp32 on top of
  *                 dx's bf16 value, rounded once; dlogits is zero off the
  *                 top-k set, so this is dlogits w_router)
- *   dw_router[e] = sum over the rows r of expert e, in sorted order, of
+ *   dw_router[e] = sum over the rows r of expert e, in a fixed order, of
  *                 dlogits[t(r), e] x[t(r)]                   (fp32, written)
  * dlogits: device [T,E] fp32 (moe_backward's); x, w_router as for
  * moe_route_project; dx: device [T,H] bf16, read and written; dw_router:
