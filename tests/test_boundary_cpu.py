@@ -199,3 +199,31 @@ def test_mxfp8_mode_dims_and_kernel_counts():
     sz = ctypes.c_size_t(0)
     bad = g.Dims.of(64, 128, 64, 8, 2, "mxfp8")            # I must be a multiple of 128
     assert lib.moe_workspace_size(ctypes.byref(bad), ctypes.byref(sz), None, None, None) == 3
+
+
+def test_router_projection_argument_errors():
+    """moe_route_project / moe_router_backward validate on the host before any
+    launch: fp32 mode unsupported, null and misaligned pointers, workspace."""
+    g, lib = _lib()
+    d = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    r = _fake_routing(g)
+    t = lambda i: _FakeTensor(0x7C0000000000 + i * 0x1000000)
+    with pytest.raises(g.MoeError) as ei:
+        g.route_project(g.Dims.of(64, 128, 64, 8, 2, "fp32"), t(0), t(1), t(2), r, t(3), stream=_NullStream())
+    assert ei.value.status == 3
+    with pytest.raises(g.MoeError) as ei:
+        g.route_project(d, t(0), None, t(2), r, t(3), stream=_NullStream())
+    assert ei.value.status == 1
+    with pytest.raises(g.MoeError) as ei:
+        g.route_project(d, t(0), _FakeTensor(0x7C0000000010), t(2), r, t(3), stream=_NullStream())
+    assert ei.value.status == 4
+    with pytest.raises(g.MoeError) as ei:
+        g.route_project(d, t(0), t(1), t(2), r, _FakeTensor(0x7B0000000000, 1), stream=_NullStream())
+    assert ei.value.status == 5
+    with pytest.raises(g.MoeError) as ei:
+        g.router_backward(d, r, t(0), t(1), t(2), None, t(4), stream=_NullStream())
+    assert ei.value.status == 1
+    with pytest.raises(g.MoeError) as ei:
+        g.router_backward(g.Dims.of(64, 128, 64, 8, 2, "fp32"), r, t(0), t(1), t(2), t(3), t(4),
+                          stream=_NullStream())
+    assert ei.value.status == 3

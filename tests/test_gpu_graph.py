@@ -56,3 +56,50 @@ def test_graph_replays_match_eager(dims, seed):
         for i, (a, b) in enumerate(zip(_outputs(L), eager)):
             assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), (rep, i)
         del scratch
+
+
+def test_graph_router_projection_replays_match_eager():
+    """route_project + forward + backward + router_backward captured in one
+    graph: every replay reproduces the eager logits, routing, layer outputs
+    and router gradient bit for bit."""
+    import torch
+    dims = mi.LayerDims(T=500, H=256, I=128, E=16, k=4, dtype="bf16")
+    print(f"[graph] router projection dims={dims}", flush=True)
+    run = GpuRun(dims, mi.make_inputs(dims, 404))
+    L = run.layer
+    rng = np.random.default_rng(405)
+    wr = torch.from_numpy(mi.bf16_round(rng.standard_normal((dims.E, dims.H)).astype(np.float32) * 0.05)).to(
+        "cuda", torch.bfloat16)
+    dwr = torch.empty((dims.E, dims.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        L.route_project(run.x, wr)
+        run.forward()
+        run.backward()
+        L.router_backward(run.x, wr, dwr)
+
+    step()
+    torch.cuda.synchronize()
+    outs = lambda: _outputs(L) + [L.logits, dwr]
+    eager = [t.clone() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs():
+            if t.dtype.is_floating_point:
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs(), eager)):
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), (rep, i)
