@@ -412,10 +412,10 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
 // Forward: 256 x 256 tiles with a 64-wide K tile (128-byte rows per DMA
 // lane group, one 8-wave block per CU): fewer operand bytes per flop and full
 // cache lines outweigh the longer ragged tail (measured 8 % faster for both
-// forward GEMMs); tile groups of 16 (2 % faster than 32).  The dgrad kinds
-// measured faster with 128 x 256, K tile 32, two 4-wave blocks per CU.
+// forward GEMMs).  The dgrad kinds measured faster with 128 x 256, K tile 32,
+// two 4-wave blocks per CU.
 #ifndef MOE_CFG_ROW_FWD
-#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64, 16
+#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64
 #endif
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
