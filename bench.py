@@ -142,6 +142,50 @@ def time_router_projection(g, layer, d, x, seed, K, W):
             "note": "logits = x W_r^T + routing; backward: dx += dlogits W_r, dW_r = dlogits^T x"}
 
 
+def vendor_ceiling(d, reps: int = 20):
+    """hipBLASLt (through torch) on the layer's per-expert GEMM shapes, as a
+    measured context for the MFMA roofline: the same expert shapes as batched
+    products with uniform rows per expert (no gather, no fused epilogue, bf16
+    output), the same flops as one dense product, and a large square product.
+    Not part of a step; the layer never calls these."""
+    import torch
+    m = d.M // d.E
+    dt = torch.bfloat16
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *s: torch.randn(*s, device="cuda", dtype=dt, generator=gen)
+
+    def timed(fn, flop):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        return {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+    out = {}
+    xb, w13b = rnd(d.E, m, d.H), rnd(d.E, d.H, 2 * d.I)      # right operands contiguous (K-outer)
+    out["bmm_gemm1_shape"] = timed(lambda: torch.bmm(xb, w13b), 2.0 * d.E * m * d.H * 2 * d.I)
+    del xb, w13b
+    ab, w2b = rnd(d.E, m, d.I), rnd(d.E, d.I, d.H)
+    out["bmm_gemm2_shape"] = timed(lambda: torch.bmm(ab, w2b), 2.0 * d.E * m * d.I * d.H)
+    del ab, w2b
+    xd, wd = rnd(d.E * m, d.H), rnd(2 * d.I, d.H)
+    out["mm_gemm1_flops_dense_nt"] = timed(lambda: xd @ wd.t(), 2.0 * d.E * m * d.H * 2 * d.I)
+    del xd, wd
+    n = 8192
+    xs, ws = rnd(n, n), rnd(n, n)
+    out["mm_square_8192_nt"] = timed(lambda: xs @ ws.t(), 2.0 * n ** 3)
+    del xs, ws
+    out["note"] = ("hipBLASLt via torch, bf16 in and out, fp32 accumulate; batched shapes use "
+                   f"{m} rows per expert; context for the practical MFMA ceiling, not part of the layer")
+    return out
+
+
 def copy_calibration(mib: int):
     """One plain device-to-device copy of `mib` MiB (bytes known exactly), for
     scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
@@ -189,6 +233,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--mode", choices=["bf16", "mxfp8", "fp8_bwd"], default=None,
                     help="run the configuration's shape in another precision mode")
+    ap.add_argument("--vendor-ceiling", action="store_true",
+                    help="also time hipBLASLt on the per-expert GEMM shapes (roofline context)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the timed region (counter calibration)")
     args = ap.parse_args()
@@ -311,6 +357,8 @@ def main():
     }
     if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
         out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
+    if args.vendor_ceiling:
+        out["vendor_ceiling"] = vendor_ceiling(d)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_tokens)
