@@ -312,13 +312,18 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
     // dA' = acc passes through LDS in fp32, CH rows at a time; then each
     // thread takes 8 consecutive columns of one row: coalesced 16-byte loads
     // of G1 and G3, stores of dG1, dG3 and g*A, and the row's gate-gradient
-    // partial summed over the 32 lanes that hold the row (fixed order).
+    // partial summed over the 32 lanes that hold the row (fixed order).  All
+    // gate and G13 loads of a chunk are issued before the chunk is staged, so
+    // their latency overlaps the LDS transpose and each other instead of
+    // stalling every row in turn.
     constexpr int NQ4 = BN / 4;                            // 16-byte fp32 chunks per row
     constexpr int TPR = BN / 8;                            // threads per row
     static_assert(TPR == 32 && NTHR % TPR == 0, "one row per half wave");
     constexpr int CH0 = C::SMEM_BYTES / (BN * 4);
     constexpr int CH = CH0 >= BM ? BM : CH0 >= 64 ? 64 : CH0 >= 32 ? 32 : 16;
     static_assert(CH * BN * 4 <= C::SMEM_BYTES && BM % CH == 0 && CH % 16 == 0, "fp32 row chunk must fit");
+    constexpr int NCH = BM / CH, IT = CH * TPR / NTHR;   // chunks per tile, rows-pieces per thread and chunk
+    static_assert(IT * NTHR == CH * TPR, "whole row pieces per thread");
     const bf16_t* G13 = static_cast<const bf16_t*>(a.G13);
     bf16_t* dG13 = static_cast<bf16_t*>(a.dG13);
     bf16_t* Ag = static_cast<bf16_t*>(a.Ag);
@@ -328,8 +333,36 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       lo = __uint_as_float(w << 16);
       hi = __uint_as_float(w & 0xFFFF0000u);
     };
+    // piece `it` of chunk ch: row (tid + it * NTHR) / TPR of the chunk,
+    // columns n0 + 8 * (tid % TPR) ..  The routing indices, then the gates
+    // and G13 of all pieces of a chunk are loaded before the chunk is staged.
+    // Loads and stores are buffer operations without branches (a piece
+    // outside the output reads zeros and stores nowhere through an
+    // out-of-range offset), so the compiler can count them and waits only
+    // for the data each piece uses.
+    const auto r_g13 = make_rsrc(G13, (uint32_t)((size_t)a.M * 2 * I * 2));
+    const auto r_dg13 = make_rsrc(dG13, (uint32_t)((size_t)a.M * 2 * I * 2));
+    const auto r_ag = make_rsrc(Ag, (uint32_t)((size_t)a.M * I * 2));
+    const auto r_part = make_rsrc(a.dgate_part, (uint32_t)((size_t)((I + BN - 1) / BN) * a.M * 4));
+    u32x4_t r1[IT], r3[IT];
+    float gt[IT];
+    int ms[IT];
 #pragma unroll
-    for (int ch = 0; ch < BM / CH; ++ch) {
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int c = tid + it * NTHR;
+        ms[it] = a.s2f[min(m0 + ch * CH + c / TPR, mlim - 1)];
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int c = tid + it * NTHR;
+        const int m = m0 + ch * CH + c / TPR, n = n0 + 8 * (c % TPR);
+        const uint32_t o1 = (m < mlim && n < I) ? (uint32_t)(((size_t)m * 2 * I + n) * 2) : OOB;
+        gt[it] = a.gate[ms[it]];
+        r1[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1, 0, 0);
+        r3[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1 == OOB ? OOB : o1 + I * 2, 0, 0);
+      }
       if (ch > 0) __syncthreads();                         // the previous chunk has been read
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -341,47 +374,48 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       }
       __syncthreads();
 #pragma unroll
-      for (int c = tid; c < CH * TPR; c += NTHR) {
+      for (int it = 0; it < IT; ++it) {
+        const int c = tid + it * NTHR;
         const int row = c / TPR, q = c % TPR;
         const int m = m0 + ch * CH + row, n = n0 + 8 * q;
         const bool ok = m < mlim && n < I;
         const f32x4_t da0 = *reinterpret_cast<const f32x4_t*>(&s_acc[off(row, 2 * q)]);
         const f32x4_t da1 = *reinterpret_cast<const f32x4_t*>(&s_acc[off(row, 2 * q + 1)]);
-        float part = 0.f;
-        if (ok) {
-          const float g = a.gate[a.s2f[m]];
-          const size_t o1 = (size_t)m * 2 * I + n;
-          const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(G13 + o1);
-          const u32x4_t r3 = *reinterpret_cast<const u32x4_t*>(G13 + o1 + I);
-          float g1[8], g3[8], dap[8], d1[8], d3[8], ag[8];
+        const float g = gt[it];
+        float g1[8], g3[8], dap[8], d1[8], d3[8], ag[8];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            unpack(r1[w], g1[2 * w], g1[2 * w + 1]);
-            unpack(r3[w], g3[2 * w], g3[2 * w + 1]);
-            dap[w] = da0[w];
-            dap[4 + w] = da1[w];
-          }
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            const float sg = sigmoid_f32(g1[v]);
-            const float silu = g1[v] * sg;
-            const float av = silu * g3[v];
-            part += dap[v] * av;
-            const float da = g * dap[v];
-            d1[v] = da * g3[v] * sg * (1.f + g1[v] * (1.f - sg));
-            d3[v] = da * silu;
-            ag[v] = g * av;
-          }
-          *reinterpret_cast<u32x4_t*>(dG13 + o1) = u32x4_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]),
-                                                            pack_bf16x2(d1[4], d1[5]), pack_bf16x2(d1[6], d1[7])};
-          *reinterpret_cast<u32x4_t*>(dG13 + o1 + I) = u32x4_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3]),
-                                                                pack_bf16x2(d3[4], d3[5]), pack_bf16x2(d3[6], d3[7])};
-          *reinterpret_cast<u32x4_t*>(Ag + (size_t)m * I + n) =
-              u32x4_t{pack_bf16x2(ag[0], ag[1]), pack_bf16x2(ag[2], ag[3]), pack_bf16x2(ag[4], ag[5]),
-                      pack_bf16x2(ag[6], ag[7])};
+        for (int w = 0; w < 4; ++w) {
+          unpack(r1[it][w], g1[2 * w], g1[2 * w + 1]);
+          unpack(r3[it][w], g3[2 * w], g3[2 * w + 1]);
+          dap[w] = da0[w];
+          dap[4 + w] = da1[w];
         }
+        float part = 0.f;                                  // a piece outside the output reads G13 = 0: adds 0
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float sg = sigmoid_f32(g1[v]);
+          const float silu = g1[v] * sg;
+          const float av = silu * g3[v];
+          part += dap[v] * av;
+          const float da = g * dap[v];
+          d1[v] = da * g3[v] * sg * (1.f + g1[v] * (1.f - sg));
+          d3[v] = da * silu;
+          ag[v] = g * av;
+        }
+        const uint32_t o1 = ok ? (uint32_t)(((size_t)m * 2 * I + n) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]),
+                                                       pack_bf16x2(d1[4], d1[5]), pack_bf16x2(d1[6], d1[7])},
+                                               r_dg13, o1, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3]),
+                                                       pack_bf16x2(d3[4], d3[5]), pack_bf16x2(d3[6], d3[7])},
+                                               r_dg13, ok ? o1 + I * 2 : OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pack_bf16x2(ag[0], ag[1]), pack_bf16x2(ag[2], ag[3]),
+                                                       pack_bf16x2(ag[4], ag[5]), pack_bf16x2(ag[6], ag[7])},
+                                               r_ag, ok ? (uint32_t)(((size_t)m * I + n) * 2) : OOB, 0, 0);
         part = fsum_lanes32(part);                         // the 32 lanes of this row
-        if ((lane & 31) == 0 && m < mlim) a.dgate_part[(size_t)(n0 / BN) * a.M + m] = part;
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(part), r_part,
+            ((lane & 31) == 0 && m < mlim) ? (uint32_t)(((size_t)(n0 / BN) * a.M + m) * 4) : OOB, 0, 0);
       }
     }
   } else {   // wgrad: fp32 output of one expert, staged through LDS so each
