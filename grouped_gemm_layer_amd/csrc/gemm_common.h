@@ -493,25 +493,48 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
   float psum[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) psum[i] = 0.f;
+  // The gates of the wave's rows are loaded up front (the routing index, then
+  // the gate), so that each 2x2 block of fragments waits only for its own
+  // G13 loads.  Rows past the expert and columns past I read in-bounds
+  // values, zeroed below.
+  int sfl[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sfl[i] = a.s2f[min(m0 + wm * WM + 16 * i + mrow, mlim - 1)];
+  float gi[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) gi[i] = a.gate[sfl[i]];
+  f32x4_t gb[2][2][2];   // [row block ii][column block jj][G1, G3]
+  auto load_g13 = [&](int ip, int jp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int mc = min(m0 + wm * WM + 16 * (2 * ip + ii) + mrow, mlim - 1);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int n = n0 + wn * WN + 16 * (2 * jp + jj) + ncol;
+        const size_t o = (size_t)mc * 2 * I + min(n, I - 4);
+        gb[ii][jj][0] = *reinterpret_cast<const f32x4_t*>(G13 + o);
+        gb[ii][jj][1] = *reinterpret_cast<const f32x4_t*>(G13 + o + I);
+      }
+    }
+  };
 
 #pragma unroll
   for (int ip = 0; ip < FM / 2; ++ip) {
 #pragma unroll
     for (int jp = 0; jp < FN / 2; ++jp) {
+      load_g13(ip, jp);
       float d[3][2][2][4];   // [dG1, dG3, g*A][row block ii][column block jj][v]; zero outside the expert / I
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * ip + ii;
         const int m = m0 + wm * WM + 16 * i + mrow;
-        const int mc = min(m, mlim - 1);                     // rows past the expert: in-bounds reads, zeroed
-        const float g = a.gate[a.s2f[mc]];
+        const float g = gi[i];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int n = n0 + wn * WN + 16 * (2 * jp + jj) + ncol;
           const bool ok = m < mlim && n < I;
-          const size_t o = (size_t)mc * 2 * I + min(n, I - 4);
-          f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(G13 + o);
-          f32x4_t g3 = *reinterpret_cast<const f32x4_t*>(G13 + o + I);
+          f32x4_t g1 = gb[ii][jj][0];
+          f32x4_t g3 = gb[ii][jj][1];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {   // zero G13 outside the tile: every derived value is then zero
             g1[v] = ok ? g1[v] : 0.f;
@@ -551,8 +574,7 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
             __builtin_amdgcn_raw_buffer_store_b32(
                 mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X), r_qdg,
                 ok ? row + 16 * jj + ncol : OOB, 0, 0);
-          if (ncol == 0)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), r_sdg, ok ? row / 32 : OOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), r_sdg, (ok && ncol == 0) ? row / 32 : OOB, 0, 0);
         }
       }
       // token blocks (32 rows = fragments 2ip, 2ip+1; 16 lanes per column), staged in LDS.
