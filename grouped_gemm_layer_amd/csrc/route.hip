@@ -21,7 +21,44 @@ constexpr int MAX_E = 512;
 
 int route_num_blocks(int M) { return (M + ROUTE_CHUNK - 1) / ROUTE_CHUNK; }
 
-// One wave per token, four tokens per block.
+// (value, expert) of the better entry: larger value, then smaller expert id;
+// id INT_MAX marks "no entry"
+__device__ __forceinline__ void take_better(float ov, int oe, float& bv, int& be) {
+  if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
+}
+// one cross-lane step of the wave arg-max through DPP (lanes paired inside rows of 16)
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& bv, int& be) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  take_better(ov, oe, bv, be);
+}
+// the gfx950 row swaps pair rows 0-1 and 2-3 (16) or halves (32); each lane
+// gets its own and its partner's value, in the same order for both words
+__device__ __forceinline__ void best_swap16(float& bv, int& be) {
+  const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+  const auto re = __builtin_amdgcn_permlane16_swap((uint32_t)be, (uint32_t)be, false, false);
+  float v = __uint_as_float(rv[0]);
+  int e = (int)re[0];
+  take_better(__uint_as_float(rv[1]), (int)re[1], v, e);
+  bv = v;
+  be = e;
+}
+__device__ __forceinline__ void best_swap32(float& bv, int& be) {
+  const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+  const auto re = __builtin_amdgcn_permlane32_swap((uint32_t)be, (uint32_t)be, false, false);
+  float v = __uint_as_float(rv[0]);
+  int e = (int)re[0];
+  take_better(__uint_as_float(rv[1]), (int)re[1], v, e);
+  bv = v;
+  be = e;
+}
+
+// One wave per token, four tokens per block.  Each of the k rounds takes the
+// best remaining entry of every lane, then the wave's best through six
+// cross-lane steps (quad swaps, the two row mirrors, the row swaps), after
+// which every lane holds the same (value, expert): the order of the
+// comparisons does not change the result, the key being a strict order.
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits, int T, int E,
                                                         int k, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate) {
@@ -44,18 +81,14 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     float bv = 0.f;
     int be = INT_MAX;
 #pragma unroll
-    for (int q = 0; q < MAX_EPL; ++q) {
-      if (live & (1u << q)) {
-        const int e = lane + 64 * q;
-        if (be == INT_MAX || v[q] > bv || (v[q] == bv && e < be)) { bv = v[q]; be = e; }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
-    }
+    for (int q = 0; q < MAX_EPL; ++q)
+      if (live & (1u << q)) take_better(v[q], lane + 64 * q, bv, be);
+    best_dpp<0xB1>(bv, be);    // quad_perm 1,0,3,2
+    best_dpp<0x4E>(bv, be);    // quad_perm 2,3,0,1
+    best_dpp<0x141>(bv, be);   // row_half_mirror
+    best_dpp<0x140>(bv, be);   // row_mirror
+    best_swap16(bv, be);
+    best_swap32(bv, be);
     if (lane == (be & 63)) live &= ~(1u << (be >> 6));
     if (j == 0) v0 = bv;
     if (lane == j) { my_v = bv; my_e = be; }
@@ -87,18 +120,26 @@ __global__ __launch_bounds__(256) void expert_hist_kernel(const int32_t* __restr
 
 // One block: counts, offsets and the expert-major block bases
 //   bases[b][e] = offsets[e] + sum_{b' < b} partials[b'][e].
+// Each thread (expert) reads its column of partials SCAN_U blocks at a time,
+// so the loads of a batch are in flight together.
+constexpr int SCAN_U = 16;
 __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __restrict__ partials, int nblk,
                                                            int E, int32_t* __restrict__ bases,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets) {
   __shared__ int s_scan[2][MAX_E];
   const int e = threadIdx.x;
+  auto load_batch = [&](int b0, int (&c)[SCAN_U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < SCAN_U; ++u) c[u] = (b0 + u < nblk) ? partials[(size_t)(b0 + u) * E + e] : 0;
+  };
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = partials[b * E + e];
-      bases[b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += SCAN_U) {
+      int c[SCAN_U];
+      load_batch(b0, c);
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) run += c[u];
     }
     counts[e] = run;
   }
@@ -119,7 +160,16 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
     const int excl = s_scan[cur][e] - run;
     offsets[e] = excl;
     if (e == E - 1) offsets[E] = s_scan[cur][e];
-    for (int b = 0; b < nblk; ++b) bases[b * E + e] += excl;
+    int pre = excl;
+    for (int b0 = 0; b0 < nblk; b0 += SCAN_U) {
+      int c[SCAN_U];
+      load_batch(b0, c);
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) {
+        if (b0 + u < nblk) bases[(size_t)(b0 + u) * E + e] = pre;
+        pre += c[u];
+      }
+    }
   }
 }
 
