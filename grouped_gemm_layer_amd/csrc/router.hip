@@ -14,19 +14,22 @@
 namespace moe {
 namespace {
 
-// One wave per 64 tokens x 64 experts, K = H in steps of 32, operands read
-// straight from global memory into MFMA fragments (the projection is 2 T E H
-// flop, a few percent of the layer; its operands stay in L2).  With
+// One block of RL_NW waves per 64 tokens x 64 experts, K = H in steps of 32:
+// wave w takes the steps w, w + RL_NW, ... and the waves' partial sums are
+// added in wave order through LDS (fixed order, fp32).  Operands are read
+// straight from global memory into MFMA fragments (the projection is
+// 2 T E H flop, a few percent of the layer; its operands stay in L2).  With
 // v_mfma_f32_16x16x32_bf16 called as mfma(P, Q, c), lane l holds
 // sum_k P[4 (l/16) + v][k] Q[l%16][k], v = 0..3, and an operand fragment is
 // row l%16, K elements 8 (l/16) .. +7: here P = W_r rows (experts) and Q = x
 // rows (tokens), so a lane ends with 4 consecutive experts of one token.
-constexpr int RL_T = 64, RL_E = 64;
+constexpr int RL_T = 64, RL_E = 64, RL_NW = 4;
 
-__global__ __launch_bounds__(64) void router_logits_kernel(const bf16_t* __restrict__ x,
-                                                           const bf16_t* __restrict__ wr, int T, int H, int E,
-                                                           float* __restrict__ logits) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * RL_NW) void router_logits_kernel(const bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ wr, int T, int H,
+                                                                   int E, float* __restrict__ logits) {
+  __shared__ f32x4_t s_acc[RL_NW - 1][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * RL_T, e0 = blockIdx.y * RL_E;
   const int r = lane & 15, kq = 8 * (lane >> 4);
   f32x4_t acc[4][4];
@@ -43,7 +46,7 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const bf16_t* __restr
     xr[i] = x + (size_t)(t < T ? t : 0) * H + kq;
     wrr[i] = wr + (size_t)(e < E ? e : 0) * H + kq;
   }
-  for (int k0 = 0; k0 < H; k0 += 32) {
+  for (int k0 = 32 * wave; k0 < H; k0 += 32 * RL_NW) {
     bf16x8_t xf[4], wf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -56,6 +59,20 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const bf16_t* __restr
       for (int j = 0; j < 4; ++j)     // expert block
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_acc[wave - 1][4 * i + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < RL_NW - 1; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += s_acc[w][4 * i + j][lane];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + 16 * i + r;
@@ -96,14 +113,21 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
       acc[2 * i] = __uint_as_float(dw[i] << 16);
       acc[2 * i + 1] = __uint_as_float(dw[i] & 0xFFFF0000u);
     }
-    for (int j = 0; j < k; ++j) {
-      const uint4 w = *reinterpret_cast<const uint4*>(wr + (size_t)s_e[j] * H + h0);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      const float g = s_d[j];
+    for (int j0 = 0; j0 < k; j0 += 8) {   // the rows of 8 slots in flight together
+      uint4 w[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += g * __uint_as_float(ww[i] << 16);
-        acc[2 * i + 1] += g * __uint_as_float(ww[i] & 0xFFFF0000u);
+      for (int u = 0; u < 8; ++u)
+        w[u] = j0 + u < k ? *reinterpret_cast<const uint4*>(wr + (size_t)s_e[j0 + u] * H + h0) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= k) break;
+        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+        const float g = s_d[j0 + u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += g * __uint_as_float(ww[i] << 16);
+          acc[2 * i + 1] += g * __uint_as_float(ww[i] & 0xFFFF0000u);
+        }
       }
     }
     *reinterpret_cast<uint4*>(dx + (size_t)t * H + h0) =
@@ -112,18 +136,21 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
   }
 }
 
-// dW_r[e][h] for one expert e (blockIdx.y) and 512 columns (8 per lane):
-// wave w of the block sums rows w, w + 4, w + 8, ... of the expert's sorted
-// rows (4 rows in flight), then the four partial sums are added in wave
-// order through LDS: fixed order, fp32.  An expert with no rows writes zeros.
-constexpr int RDW_COLS = 512;
+// dW_r[e][h] for one expert e (blockIdx.y) and 512 columns (8 per lane).
+// The expert's sorted rows go in batches of RDW_RB: batch b belongs to wave
+// b % RDW_NW, which sums its batches in order and each batch's rows in order;
+// the waves' partial sums are then added in wave order through LDS (fixed
+// order, fp32).  Per batch, lanes 0..RDW_RB-1 load the rows' token indices and
+// dlogits in one instruction each, and all RDW_RB x rows are in flight
+// together.  An expert with no rows writes zeros.
+constexpr int RDW_COLS = 512, RDW_NW = 8, RDW_RB = 16;
 
-__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dlogits,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ s2f,
-                                                        const bf16_t* __restrict__ x, int k, int H, int E,
-                                                        float* __restrict__ dwr) {
-  __shared__ __attribute__((aligned(16))) float s_part[3][RDW_COLS];
+__global__ __launch_bounds__(64 * RDW_NW) void router_dw_kernel(const float* __restrict__ dlogits,
+                                                                const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ s2f,
+                                                                const bf16_t* __restrict__ x, int k, int H, int E,
+                                                                float* __restrict__ dwr) {
+  __shared__ __attribute__((aligned(16))) float s_part[RDW_NW - 1][RDW_COLS];
   const int e = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = blockIdx.x * RDW_COLS + 8 * lane;
@@ -132,31 +159,26 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  auto add_row = [&](uint4 v, float d) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int rb = r0 + wave * RDW_RB; rb < r1; rb += RDW_NW * RDW_RB) {
+    const int rr = rb + (lane & (RDW_RB - 1));
+    const int tl = rr < r1 ? s2f[rr] / k : -1;            // lane u < RDW_RB: token of row rb + u
+    const float dl = tl >= 0 ? dlogits[(size_t)tl * E + e] : 0.f;
+    uint4 v[RDW_RB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += d * __uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += d * __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  };
-  int r = r0 + wave;
-  for (; r + 12 < r1; r += 16) {   // rows r, r+4, r+8, r+12 of this wave
-    uint4 v[4];
-    float d[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = s2f[r + 4 * u] / k;
-      d[u] = dlogits[(size_t)t * E + e];
-      v[u] = live ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < RDW_RB; ++u) {
+      const int t = __builtin_amdgcn_readlane(tl, u);
+      v[u] = (t >= 0 && live) ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add_row(v[u], d[u]);
-  }
-  for (; r < r1; r += 4) {
-    const int t = s2f[r] / k;
-    add_row(live ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0) : make_uint4(0u, 0u, 0u, 0u),
-            dlogits[(size_t)t * E + e]);
+    for (int u = 0; u < RDW_RB; ++u) {
+      const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), u));
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += d * __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] += d * __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
   }
   if (wave > 0) {
 #pragma unroll
@@ -165,7 +187,7 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
   __syncthreads();
   if (wave == 0 && live) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < RDW_NW - 1; ++w)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += s_part[w][8 * lane + i];
     float* dst = dwr + (size_t)e * H + h0;
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
 
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* wr, int T, int H, int E, float* logits,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(router_logits_kernel, dim3((T + RL_T - 1) / RL_T, (E + RL_E - 1) / RL_E), dim3(64), 0, s, x,
+  hipLaunchKernelGGL(router_logits_kernel, dim3((T + RL_T - 1) / RL_T, (E + RL_E - 1) / RL_E), dim3(64 * RL_NW), 0, s, x,
                      wr, T, H, E, logits);
   return hipGetLastError();
 }
@@ -189,7 +211,7 @@ hipError_t launch_router_project_bwd(const float* dlogits, const int32_t* topk_i
   hipLaunchKernelGGL(router_dx_kernel, dim3(T), dim3(256), 0, s, dlogits, topk_idx, wr, k, H, E, dx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_dw_kernel, dim3((H + RDW_COLS - 1) / RDW_COLS, E), dim3(256), 0, s, dlogits, offsets,
+  hipLaunchKernelGGL(router_dw_kernel, dim3((H + RDW_COLS - 1) / RDW_COLS, E), dim3(64 * RDW_NW), 0, s, dlogits, offsets,
                      s2f, x, k, H, E, dwr);
   return hipGetLastError();
 }
