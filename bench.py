@@ -142,6 +142,23 @@ def time_router_projection(g, layer, d, x, seed, K, W):
             "note": "logits = x W_r^T + routing; backward: dx += dlogits W_r, dW_r = dlogits^T x"}
 
 
+def time_backward_accumulate(layer, dy, x, w13, w2, K, W):
+    """moe_backward_accumulate (weight gradients added into the fp32 buffers)
+    on the same batch, after the timed steps (not part of a step)."""
+    import numpy as np
+    import torch
+    for _ in range(W):
+        layer.backward(dy, x, w13, w2, accumulate=True)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        layer.backward(dy, x, w13, w2, accumulate=True)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return round(float(np.mean([e[0].elapsed_time(e[1]) for e in ev])), 4)
+
+
 def vendor_ceiling(d, reps: int = 20):
     """hipBLASLt (through torch) on the layer's per-expert GEMM shapes, as a
     measured context for the MFMA roofline: the same expert shapes as batched
@@ -357,6 +374,8 @@ def main():
     }
     if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
         out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
+    # the backward with the weight gradients added into fp32 main-gradient buffers, timed on its own
+    out["bwd_accumulate_ms"] = time_backward_accumulate(layer, dy, x, w13, w2, K, W)
     if args.vendor_ceiling:
         out["vendor_ceiling"] = vendor_ceiling(d)
     if not args.no_cpu_baseline:

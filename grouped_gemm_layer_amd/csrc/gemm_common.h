@@ -443,13 +443,31 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         }
       }
       __syncthreads();
-      for (int c = tid; c < CH * NQ; c += NTHR) {
-        const int row = c / NQ, q = c % NQ;
-        const int m = m0 + ch * CH + row, n = n0 + 4 * q;
-        if (m < mlim && n < nlim) {
-          f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]);
-          if (wacc) v = *reinterpret_cast<const f32x4_t*>(out + (size_t)m * ld + n) + v;   // accumulate-into
-          st_out<true>(out + (size_t)m * ld + n, v);
+      constexpr int IT = CH * NQ / NTHR;                   // 16-byte pieces per thread and chunk
+      static_assert(IT * NTHR == CH * NQ, "whole pieces per thread");
+      if (wacc) {   // accumulate-into: every old value of the chunk is loaded before the first store
+        f32x4_t old[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int c = tid + it * NTHR, row = c / NQ, q = c % NQ;
+          const int m = m0 + ch * CH + row, n = n0 + 4 * q;
+          old[it] = (m < mlim && n < nlim) ? *reinterpret_cast<const f32x4_t*>(out + (size_t)m * ld + n)
+                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int c = tid + it * NTHR, row = c / NQ, q = c % NQ;
+          const int m = m0 + ch * CH + row, n = n0 + 4 * q;
+          if (m < mlim && n < nlim)
+            st_out<true>(out + (size_t)m * ld + n, old[it] + *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int c = tid + it * NTHR, row = c / NQ, q = c % NQ;
+          const int m = m0 + ch * CH + row, n = n0 + 4 * q;
+          if (m < mlim && n < nlim)
+            st_out<true>(out + (size_t)m * ld + n, *reinterpret_cast<const f32x4_t*>(&s_out[out_off(row, q)]));
         }
       }
     }
