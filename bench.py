@@ -250,6 +250,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--mode", choices=["bf16", "mxfp8", "fp8_bwd"], default=None,
                     help="run the configuration's shape in another precision mode")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router projection and accumulate-into timings that follow the steps "
+                         "(profiled runs: every GEMM launch is then a plain step's)")
     ap.add_argument("--vendor-ceiling", action="store_true",
                     help="also time hipBLASLt on the per-expert GEMM shapes (roofline context)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -372,10 +375,11 @@ def main():
         "gemm_mfma_frac": round(sum(flops[n] / (peak[n] * 1e12) for n in flops) / (gemm_ms * 1e-3), 4),
         "kernels": kernels, "roofline": roofline, "cpu_baseline": None,
     }
-    if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
-        out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
-    # the backward with the weight gradients added into fp32 main-gradient buffers, timed on its own
-    out["bwd_accumulate_ms"] = time_backward_accumulate(layer, dy, x, w13, w2, K, W)
+    if not args.no_extras:
+        if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
+            out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
+        # the backward with the weight gradients added into fp32 main-gradient buffers, timed on its own
+        out["bwd_accumulate_ms"] = time_backward_accumulate(layer, dy, x, w13, w2, K, W)
     if args.vendor_ceiling:
         out["vendor_ceiling"] = vendor_ceiling(d)
     if not args.no_cpu_baseline:
