@@ -94,7 +94,13 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   if (lane < k) {
     const size_t f = (size_t)t * k + lane;
     const int r = f2s[f];
-    for (int p = 0; p < n_parts; ++p) dg += part[(size_t)p * M + r];
+    for (int p0 = 0; p0 < n_parts; p0 += 4) {   // the partials of 4 column tiles in flight together
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = p0 + u < n_parts ? part[(size_t)(p0 + u) * M + r] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dg += v[u];                  // p ascending
+    }
     g = gate[f];
     e = idx[f];
     dgate[f] = dg;
@@ -108,9 +114,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int ee = e0 + lane;
     float val = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int ej = __shfl(e, j);
-      const float vj = __shfl(mine, j);
+    for (int j = 0; j < k; ++j) {   // slot j's expert and value, read as scalars from lane j
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), j));
       if (ej == ee) val = vj;
     }
     if (ee < E) row[ee] = val;

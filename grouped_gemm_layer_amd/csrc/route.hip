@@ -276,15 +276,27 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
       s_nch[rank] = c > WG_KC ? (c + WG_KC - 1) / WG_KC : 1;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {                 // E <= 512: a serial prefix over the ranks
-      int cs = 0, sl = 0;
-      for (int r = 0; r < E; ++r) {
-        wg.cstart[r] = cs;
-        wg.slot0[r] = sl;
-        cs += s_nch[r];
-        sl += s_nch[r] - 1;
+    // exclusive prefix of the chunk counts over the ranks (Hillis-Steele over
+    // MAX_E entries; ranks past E count 0): cstart[r], and slot0[r] =
+    // cstart[r] - r (chunks beyond each rank's first)
+    __shared__ int s_cs[2][MAX_E];
+    int cc = 0;
+    if (e < MAX_E) s_cs[0][e] = (e < E) ? s_nch[e] : 0;
+    __syncthreads();
+    for (int off = 1; off < MAX_E; off <<= 1) {
+      if (e < MAX_E) {
+        int val = s_cs[cc][e];
+        if (e >= off) val += s_cs[cc][e - off];
+        s_cs[cc ^ 1][e] = val;
       }
-      wg.cstart[E] = cs;
+      cc ^= 1;
+      __syncthreads();
+    }
+    if (e < E) {
+      const int excl = s_cs[cc][e] - s_nch[e];
+      wg.cstart[e] = excl;
+      wg.slot0[e] = excl - e;
+      if (e == E - 1) wg.cstart[E] = s_cs[cc][e];
     }
   }
   // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
