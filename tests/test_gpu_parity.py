@@ -163,3 +163,23 @@ def test_determinism_bitwise():
     import torch
     for a, b in zip(*outs):
         assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("T,E,k,ties,seed", [
+    (3000, 512, 32, False, 120),   # 8 logits per lane, 24 scan blocks (a full and a partial batch of 16)
+    (3000, 512, 32, True, 121),    # the same with many ties at the top-k boundary
+    (5000, 96, 5, False, 122),     # lanes 32..63 hold one logit
+    (700, 8, 8, True, 123),        # k = E < 64: most lanes hold none
+])
+def test_route_extremes_exact(T, E, k, ties, seed):
+    """Routing at the ends of the supported range (E up to 512, k up to 32)
+    matches the oracle bit for bit: the wave arg-max over (value, expert)
+    pairs and the batched expert scan."""
+    d = mi.LayerDims(T=T, H=64, I=64, E=E, k=k, dtype="bf16")
+    print(f"[parity] route T={T} E={E} k={k} ties={ties}", flush=True)
+    inp = mi.make_inputs(d, seed)
+    if ties:
+        inp["logits"] = np.round(inp["logits"] * 2.0).astype(np.float32) / 2.0
+    run = GpuRun(d, inp)
+    run.route()
+    check_routing_exact(run.routing_np(), orc.route(inp["logits"], d.k))
