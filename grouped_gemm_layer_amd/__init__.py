@@ -91,6 +91,9 @@ def load_library():
     lib.moe_router_backward.restype = ctypes.c_int
     lib.moe_backward_accumulate.argtypes = lib.moe_backward.argtypes
     lib.moe_backward_accumulate.restype = ctypes.c_int
+    lib.moe_forward_recompute.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, ctypes.POINTER(_CRouting), vp, vp, sz,
+                                          vp]
+    lib.moe_forward_recompute.restype = ctypes.c_int
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [vp, ctypes.c_int]
     lib.moe_backward_timed.argtypes = lib.moe_backward.argtypes + [vp, ctypes.c_int]
     lib.moe_forward_timed.restype = ctypes.c_int
@@ -198,6 +201,14 @@ def forward(dims: Dims, x, w13, w2, routing: RoutingBuffers, y, saved, ws, strea
         _check(lib.moe_forward_timed(*args, events, len(events)), "moe_forward_timed")
 
 
+def forward_recompute(dims: Dims, x, w13, w2, routing: RoutingBuffers, saved, ws, stream=None):
+    """moe_forward_recompute: restore `saved` for the backward without computing y."""
+    lib = load_library()
+    r = routing.c()
+    _check(lib.moe_forward_recompute(ctypes.byref(dims), _ptr(x), _ptr(w13), _ptr(w2), ctypes.byref(r),
+                                     _ptr(saved), _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_recompute")
+
+
 def backward(dims: Dims, dy, x, w13, w2, routing: RoutingBuffers, saved, dx, dw13, dw2, dgate, dlogits, ws,
              stream=None, events=None, accumulate=False):
     """events: optional ctypes array of hipEvent_t (moe_backward_timed).
@@ -287,6 +298,10 @@ class MoeLayer:
     def forward(self, x, w13, w2, stream=None, events=None):
         forward(self.dims, x, w13, w2, self.routing, self.y, self.saved, self.fwd_ws, stream, events)
         return self.y
+
+    def forward_recompute(self, x, w13, w2, stream=None):
+        """Second forward of activation checkpointing: `saved` as forward() writes it, y untouched."""
+        forward_recompute(self.dims, x, w13, w2, self.routing, self.saved, self.fwd_ws, stream)
 
     def backward(self, dy, x, w13, w2, want_dlogits=True, stream=None, events=None, accumulate=False):
         backward(self.dims, dy, x, w13, w2, self.routing, self.saved, self.dx, self.dw13, self.dw2, self.dgate,

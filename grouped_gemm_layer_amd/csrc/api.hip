@@ -216,7 +216,7 @@ inline int backward_kernels(int mode) {
 
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
-                        hipStream_t stream, Marks mk);
+                        hipStream_t stream, Marks mk, bool recompute = false);
 moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,
                          const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
                          float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk,
@@ -294,13 +294,15 @@ moe_status moe_router_backward(const moe_dims* dims, const moe_routing* routing,
 
 namespace {
 
+// recompute: the second forward of activation checkpointing, which restores
+// `saved` for the backward and skips what only produces y (GEMM W2, combine)
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
-                        hipStream_t stream, Marks mk) {
+                        hipStream_t stream, Marks mk, bool recompute) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_routing(routing)) != MOE_OK) return st;
-  if (!x || !w13 || !w2 || !y || !saved || !ws) return MOE_ERR_NULL;
+  if (!x || !w13 || !w2 || (!y && !recompute) || !saved || !ws) return MOE_ERR_NULL;
   if (!aligned(x) || !aligned(w13) || !aligned(w2) || !aligned(y) || !aligned(saved) || !aligned(ws))
     return MOE_ERR_ALIGN;
   const Sizes s = compute_sizes(dims);
@@ -339,15 +341,15 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
       step(launch_mx_quant_both(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, svp(s.sv_qw13t),
                                 svp(s.sv_sw13t), u8(s.f_qw13), u8(s.f_sw13), stream));
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
-    if (e == hipSuccess)
+    if (e == hipSuccess)   // the transposed W2 copy in `saved` is the backward's, so the recompute keeps it
       step(launch_mx_quant_both(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, svp(s.sv_qw2t), svp(s.sv_sw2t),
                                 u8(s.f_qw2), u8(s.f_sw2), stream));
-    if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
+    if (e == hipSuccess && !recompute) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
   } else {
     if (e == hipSuccess) step(gemm(bf16, KIND_FWD1, a, stream));
-    if (e == hipSuccess) step(gemm(bf16, KIND_FWD2, a, stream));
+    if (e == hipSuccess && !recompute) step(gemm(bf16, KIND_FWD2, a, stream));
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !recompute) {
     if (bf16)
       e = launch_combine<bf16_t>(static_cast<const bf16_t*>(a.O), a.f2s, a.gate, a.T, a.k, a.H,
                                  static_cast<bf16_t*>(y), stream);
@@ -463,6 +465,13 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, con
                        const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
   return forward_impl(dims, x, w13, w2, routing, y, saved, ws, ws_bytes, stream, Marks{nullptr, 0, 0, stream});
+}
+
+moe_status moe_forward_recompute(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                                 const moe_routing* routing, void* saved, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return forward_impl(dims, x, w13, w2, routing, nullptr, saved, ws, ws_bytes, stream,
+                      Marks{nullptr, 0, 0, stream}, true);
 }
 
 moe_status moe_backward(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,

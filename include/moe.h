@@ -149,6 +149,18 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, con
                        const moe_routing* routing, void* y, void* saved,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The second forward of activation checkpointing (Prime Mega MoE news page,
+ * "How fast is Prime Mega MoE?": the training runs use full activation
+ * checkpointing, and the full-layer timing counts the forward twice).  Writes
+ * `saved` exactly as moe_forward does (bit for bit, for a moe_backward that
+ * follows) but no y: GEMM W2 and the combine, which only produce y, are
+ * skipped (in MOE_MODE_MXFP8, W2 is still quantised, since `saved` holds its
+ * transposed copy for the backward).  Arguments, sizes and errors as for
+ * moe_forward without y; routing must be the one the first forward used. */
+moe_status moe_forward_recompute(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                                 const moe_routing* routing, void* saved,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Backward pass of <dy, y> (neurobober digest, "Overlapping Backward Pass":
  * the activation-gradient chain needs only the weights; the weight gradients
  * are independent of it).

@@ -128,9 +128,22 @@ def test_forward_backward_argument_errors():
         g.backward(d, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), t(7), t(8), None,
                    _FakeTensor(0x7B0000000000, 1), stream=_NullStream(), accumulate=True)
     assert ei.value.status == 5
+    # the checkpointing recompute has moe_forward's checks, without y
+    with pytest.raises(g.MoeError) as ei:
+        g.forward_recompute(d, t(0), t(1), None, r, t(4), t(5), stream=_NullStream())
+    assert ei.value.status == 1
+    with pytest.raises(g.MoeError) as ei:
+        g.forward_recompute(d, t(0), t(1), t(2), r, t(4), _FakeTensor(0x7B0000000000, 255), stream=_NullStream())
+    assert ei.value.status == 5
+    with pytest.raises(g.MoeError) as ei:
+        g.forward_recompute(d, _FakeTensor(0x7C0000000010), t(1), t(2), r, t(4), t(5), stream=_NullStream())
+    assert ei.value.status == 4
     for dbad in (g.Dims.of(64, 128, 64, 8, 2, "mxfp8"), g.Dims.of(64, 192, 64, 8, 2, "fp8_bwd")):
         with pytest.raises(g.MoeError) as ei:
             g.forward(dbad, t(0), t(1), t(2), r, t(3), t(4), t(5), stream=_NullStream())
+        assert ei.value.status == 3
+        with pytest.raises(g.MoeError) as ei:
+            g.forward_recompute(dbad, t(0), t(1), t(2), r, t(4), t(5), stream=_NullStream())
         assert ei.value.status == 3
         with pytest.raises(g.MoeError) as ei:
             g.backward(dbad, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), t(7), t(8), None, t(9),
