@@ -312,7 +312,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   a.x = x; a.w13 = w13; a.w2 = w2;
   a.G13 = saved;
   a.g13_f32 = mx8_backward(dims->mode);
-  a.A = mx8_forward(dims->mode) ? nullptr : at(ws, s.f_A);
+  a.A = (mx8_forward(dims->mode) || recompute) ? nullptr : at(ws, s.f_A);
   a.O = at(ws, s.f_O);
   int32_t* te = reinterpret_cast<int32_t*>(at(ws, s.f_tile_e));
   int32_t* tr = reinterpret_cast<int32_t*>(at(ws, s.f_tile_r));
@@ -332,7 +332,7 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     q.qx = u8(s.f_qx);     q.sx = u8(s.f_sx);
     q.qw13 = u8(s.f_qw13); q.sw13 = u8(s.f_sw13);
     q.qa = u8(s.f_qa);     q.sa = u8(s.f_sa);
-    a.q_a = u8(s.f_qa);    a.q_sa = u8(s.f_sa);
+    if (!recompute) { a.q_a = u8(s.f_qa); a.q_sa = u8(s.f_sa); }
     q.qw2 = u8(s.f_qw2);   q.sw2 = u8(s.f_sw2);
     const bf16_t* x16 = static_cast<const bf16_t*>(x);
     if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));

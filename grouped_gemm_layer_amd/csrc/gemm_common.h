@@ -274,7 +274,9 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       staged_store<C, FH>(smem, [&](int i, int j) { return gv(i, j + FH); }, G13 + I, ld13, m0, mlim, c0, I, tid,
                           lane, wm, wn);
     }
+    // A feeds only the GEMM W2: the checkpointing recompute passes no A buffer
     if constexpr (MX8) {
+      if (a.q_a == nullptr) return;
       // MXFP8 operand of the GEMM W2 straight from fp32: blocks of 32 along I
       // are fragment pairs (2jb, 2jb+1); the 4 lanes sharing a row reduce the
       // block maximum with row swaps, codes leave through LDS along rows and
@@ -300,9 +302,10 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       }
       staged_store<C, FH>(smem, [&](int i, int j) { const f32x4_t v = av(i, j); return mx_pack4(v[0], v[1], v[2], v[3], X[i][j / 2]); },
                           static_cast<uint8_t*>(a.q_a), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
-    } else
+    } else if (a.A != nullptr) {
       staged_store<C, FH>(smem, [&](int i, int j) { const f32x4_t v = av(i, j); return pack4(v[0], v[1], v[2], v[3]); },
                           static_cast<bf16_t*>(a.A), (size_t)I, m0, mlim, c0, I, tid, lane, wm, wn);
+    }
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
     bf16_t* out = static_cast<bf16_t*>(KIND == KIND_FWD2 ? a.O : a.dXp);
     staged_store<C, FN>(smem, [&](int i, int j) { const f32x4_t v = acc[i][j]; return pack4(v[0], v[1], v[2], v[3]); },

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void gemm_fp32_kernel(LayerArgs a, int n_tiles
       const float g1 = sC[mm][c], g3 = sC[mm][BN / 2 + c];
       G13[(size_t)m * 2 * I + col] = g1;
       G13[(size_t)m * 2 * I + I + col] = g3;
-      Aout[(size_t)m * I + col] = g1 * sigmoid_f32(g1) * g3;
+      if (Aout != nullptr) Aout[(size_t)m * I + col] = g1 * sigmoid_f32(g1) * g3;   // none in the recompute
     }
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {
     float* out = static_cast<float*>(KIND == KIND_FWD2 ? a.O : a.dXp);
