@@ -142,18 +142,17 @@ def time_router_projection(g, layer, d, x, seed, K, W):
             "note": "logits = x W_r^T + routing; backward: dx += dlogits W_r, dW_r = dlogits^T x"}
 
 
-def time_forward_recompute(layer, x, w13, w2, K, W):
-    """moe_forward_recompute (the second forward of activation checkpointing:
-    the saved state only, no y) on the same batch, after the timed steps."""
+def time_call(fn, K, W):
+    """Mean event time of fn() over K calls after W untimed ones (current stream)."""
     import numpy as np
     import torch
     for _ in range(W):
-        layer.forward_recompute(x, w13, w2)
+        fn()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
         ev[i][0].record()
-        layer.forward_recompute(x, w13, w2)
+        fn()
         ev[i][1].record()
     torch.cuda.synchronize()
     return round(float(np.mean([e[0].elapsed_time(e[1]) for e in ev])), 4)
@@ -397,10 +396,13 @@ def main():
             out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
         # the backward with the weight gradients added into fp32 main-gradient buffers, timed on its own
         out["bwd_accumulate_ms"] = time_backward_accumulate(layer, dy, x, w13, w2, K, W)
-        # activation checkpointing: route + forward + recompute (saved state only) + backward
-        rec = time_forward_recompute(layer, x, w13, w2, K, W)
+        # activation checkpointing: route + forward keeping no state + recompute (the saved
+        # state only, no y) + backward
+        nosave = time_call(lambda: layer.forward(x, w13, w2, keep_saved=False), K, W)
+        rec = time_call(lambda: layer.forward_recompute(x, w13, w2), K, W)
+        out["fwd_nosave_ms"] = nosave
         out["fwd_recompute_ms"] = rec
-        out["ms_checkpointed_step"] = round(out["route_ms"] + out["fwd_ms"] + rec + out["bwd_ms"], 4)
+        out["ms_checkpointed_step"] = round(out["route_ms"] + nosave + rec + out["bwd_ms"], 4)
     if args.vendor_ceiling:
         out["vendor_ceiling"] = vendor_ceiling(d)
     if not args.no_cpu_baseline:

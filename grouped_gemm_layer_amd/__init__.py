@@ -295,8 +295,10 @@ class MoeLayer:
         """After backward(want_dlogits=True): dx += dlogits w_router, dw_router = dlogits^T x."""
         router_backward(self.dims, self.routing, self.dlogits, x, w_router, self.dx, dw_router, stream)
 
-    def forward(self, x, w13, w2, stream=None, events=None):
-        forward(self.dims, x, w13, w2, self.routing, self.y, self.saved, self.fwd_ws, stream, events)
+    def forward(self, x, w13, w2, stream=None, events=None, keep_saved=True):
+        """keep_saved=False: keep no state for a backward (checkpointing's first forward)."""
+        forward(self.dims, x, w13, w2, self.routing, self.y, self.saved if keep_saved else None, self.fwd_ws,
+                stream, events)
         return self.y
 
     def forward_recompute(self, x, w13, w2, stream=None):

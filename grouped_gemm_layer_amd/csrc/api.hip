@@ -302,7 +302,8 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_routing(routing)) != MOE_OK) return st;
-  if (!x || !w13 || !w2 || (!y && !recompute) || !saved || !ws) return MOE_ERR_NULL;
+  // saved may be NULL (not in the recompute): the forward then keeps nothing for a backward
+  if (!x || !w13 || !w2 || (!y && !recompute) || (!saved && recompute) || !ws) return MOE_ERR_NULL;
   if (!aligned(x) || !aligned(w13) || !aligned(w2) || !aligned(y) || !aligned(saved) || !aligned(ws))
     return MOE_ERR_ALIGN;
   const Sizes s = compute_sizes(dims);
@@ -337,13 +338,19 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     const bf16_t* x16 = static_cast<const bf16_t*>(x);
     if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));
     auto svp = [&](size_t off) { return static_cast<uint8_t*>(saved) + off; };
-    if (e == hipSuccess)
-      step(launch_mx_quant_both(static_cast<const bf16_t*>(w13), a.E, 2 * a.I, a.H, svp(s.sv_qw13t),
-                                svp(s.sv_sw13t), u8(s.f_qw13), u8(s.f_sw13), stream));
+    // each weight quantised both ways (the transposed copy, for the backward,
+    // into `saved`), or only along its rows when nothing is kept
+    auto quant_w = [&](const void* w, int rows_per_e, int cols, size_t sv_q, size_t sv_s, size_t f_q, size_t f_s) {
+      const bf16_t* w16 = static_cast<const bf16_t*>(w);
+      if (saved)
+        step(launch_mx_quant_both(w16, a.E, rows_per_e, cols, svp(sv_q), svp(sv_s), u8(f_q), u8(f_s), stream));
+      else
+        step(launch_mx_quant_rows(w16, a.E * rows_per_e, cols, nullptr, 1, u8(f_q), u8(f_s), stream));
+    };
+    if (e == hipSuccess) quant_w(w13, 2 * a.I, a.H, s.sv_qw13t, s.sv_sw13t, s.f_qw13, s.f_sw13);
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
-    if (e == hipSuccess)   // the transposed W2 copy in `saved` is the backward's, so the recompute keeps it
-      step(launch_mx_quant_both(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, svp(s.sv_qw2t), svp(s.sv_sw2t),
-                                u8(s.f_qw2), u8(s.f_sw2), stream));
+    // the transposed W2 copy in `saved` is the backward's, so the recompute keeps it
+    if (e == hipSuccess) quant_w(w2, a.H, a.I, s.sv_qw2t, s.sv_sw2t, s.f_qw2, s.f_sw2);
     if (e == hipSuccess && !recompute) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
   } else {
     if (e == hipSuccess) step(gemm(bf16, KIND_FWD1, a, stream));

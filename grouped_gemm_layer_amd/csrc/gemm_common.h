@@ -263,7 +263,9 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
       return f32x4_t{g1[0] * sigmoid_f32(g1[0]) * g3[0], g1[1] * sigmoid_f32(g1[1]) * g3[1],
                      g1[2] * sigmoid_f32(g1[2]) * g3[2], g1[3] * sigmoid_f32(g1[3]) * g3[3]};
     };
-    if (a.g13_f32) {   // saved state kept in fp32 (the MXFP8 backward quantises from it)
+    // G13 is the state the backward reads: none when the forward keeps nothing
+    if (a.G13 == nullptr) {
+    } else if (a.g13_f32) {   // saved state kept in fp32 (the MXFP8 backward quantises from it)
       float* G13 = static_cast<float*>(a.G13);
       staged_store<C, FH>(smem, [&](int i, int j) { return acc[i][j]; }, G13, ld13, m0, mlim, c0, I, tid, lane, wm, wn);
       staged_store<C, FH>(smem, [&](int i, int j) { return acc[i][j + FH]; }, G13 + I, ld13, m0, mlim, c0, I, tid,

@@ -119,8 +119,10 @@ __global__ __launch_bounds__(256) void gemm_fp32_kernel(LayerArgs a, int n_tiles
       const int m = m0 + mm, col = n0 + c;
       if (m >= mlim || col >= I) continue;
       const float g1 = sC[mm][c], g3 = sC[mm][BN / 2 + c];
-      G13[(size_t)m * 2 * I + col] = g1;
-      G13[(size_t)m * 2 * I + I + col] = g3;
+      if (G13 != nullptr) {   // none when the forward keeps no state for a backward
+        G13[(size_t)m * 2 * I + col] = g1;
+        G13[(size_t)m * 2 * I + I + col] = g3;
+      }
       if (Aout != nullptr) Aout[(size_t)m * I + col] = g1 * sigmoid_f32(g1) * g3;   // none in the recompute
     }
   } else if constexpr (KIND == KIND_FWD2 || KIND == KIND_DGRAD1) {

@@ -144,7 +144,13 @@ moe_status moe_router_backward(const moe_dims* dims, const moe_routing* routing,
  * ways: the forward's row-wise copy, and the transposed copy of the backward
  * (W13 along 2I, W2 along H), which goes into `saved`; in this mode
  * moe_backward takes its weight operands from `saved` and reads w13/w2 only
- * through it, so the weights must not change between the two calls. */
+ * through it, so the weights must not change between the two calls.
+ *
+ * saved may be NULL: the forward then keeps no state for a backward (G13 is
+ * not stored; in MOE_MODE_MXFP8 the weights are quantised only along their
+ * rows, for the forward's own GEMMs) and y is the same, bit for bit.  This is
+ * the first forward of activation checkpointing, whose backward follows a
+ * moe_forward_recompute. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                        const moe_routing* routing, void* y, void* saved,
                        void* ws, size_t ws_bytes, hipStream_t stream);
