@@ -103,3 +103,49 @@ def test_graph_router_projection_replays_match_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs(), eager)):
             assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), (rep, i)
+
+
+@pytest.mark.parametrize("dims,seed", [
+    (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True), 406),
+    (mi.LayerDims(T=500, H=256, I=128, E=8, k=4, dtype="bf16", mode="mxfp8"), 407),
+])
+def test_graph_checkpointed_step_replays_match_eager(dims, seed):
+    """The activation-checkpointing sequence (route, forward keeping no state,
+    recompute, backward) captured in one graph: every replay reproduces the
+    eager outputs of a plain route + forward + backward bit for bit, with the
+    saved state poisoned before each replay."""
+    import torch
+    print(f"[graph] checkpointed step dims={dims}", flush=True)
+    run = GpuRun(dims, mi.make_inputs(dims, seed))
+    run.run_all()
+    L = run.layer
+    eager = [t.clone() for t in _outputs(L)]
+
+    def step():
+        run.route()
+        L.forward(run.x, run.w13, run.w2, keep_saved=False)
+        L.forward_recompute(run.x, run.w13, run.w2)
+        run.backward()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in _outputs(L):
+            if t.dtype.is_floating_point:
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+        L.saved.view(torch.uint8).fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(_outputs(L), eager)):
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), (rep, i)
