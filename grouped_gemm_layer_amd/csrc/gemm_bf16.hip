@@ -388,18 +388,33 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     // MFMAs run from registers.
     AFrag af;
     BFrag bfr;
+    // A wave whose rows all lie past the expert's end (the ragged last tile)
+    // computes nothing it would store: it keeps its share of the DMA and the
+    // barriers and skips its fragment reads and MFMAs.
+    const bool idle = K_::ragged_rows && __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
     int st_c = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      vm_wait<(S - 1) * (DA + DB)>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      load_frags(st_c, af, bfr);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      refill_tok(kt + S);
-      mfmas_dma(af, bfr, kt + S, st_c);
-      st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+    if (idle) {
+      for (int kt = 0; kt < nk; ++kt) {
+        vm_wait<(S - 1) * (DA + DB)>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_tile(kt + S, st_c);
+        st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
+        vm_wait<(S - 1) * (DA + DB)>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load_frags(st_c, af, bfr);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        refill_tok(kt + S);
+        mfmas_dma(af, bfr, kt + S, st_c);
+        st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+      }
     }
   }
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
