@@ -260,17 +260,34 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
 #pragma unroll
   for (int st = 0; st < S; ++st) issue_tile(st, st);
   int st_c = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    vm_wait<(S - 1) * PER_WAVE>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    load_frags(st_c);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue_tile(kt + S, st_c);
-    mfmas();
-    st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+  // a wave whose rows all lie past the expert's end (the ragged last tile)
+  // keeps its share of the DMA and the barriers and skips its fragment reads
+  // and MFMAs: its accumulators stay zero, which the epilogues read as the
+  // zero rows of the padded tile
+  const bool idle = MxKind<KIND>::ragged_rows &&
+                    __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
+  if (idle) {
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<(S - 1) * PER_WAVE>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_tile(kt + S, st_c);
+      st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<(S - 1) * PER_WAVE>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      load_frags(st_c);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_tile(kt + S, st_c);
+      mfmas();
+      st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+    }
   }
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
