@@ -74,9 +74,10 @@ struct LayerArgs {
   const void* dy;                 // [T,H]
   // forward intermediates / outputs
   int g13_f32;                    // G13 stored in fp32 (the MXFP8 backward) instead of the activation type
-  void* G13;                      // [M,2I]  (saved)
-  void* A;                        // [M,I]
-  uint8_t* q_a;                   // mxfp8 mode: MXFP8 codes of A [M,I] (written by the GEMM W13 epilogue)
+  void* G13;                      // [M,2I]  (saved; null when the forward keeps no state)
+  void* A;                        // [M,I]   (null in the checkpointing recompute and in mxfp8 mode)
+  uint8_t* q_a;                   // mxfp8 mode: MXFP8 codes of A [M,I] (written by the GEMM W13 epilogue;
+                                  //   null in the checkpointing recompute, which runs no GEMM W2)
   uint8_t* q_sa;                  //   and their scales [M,I/32]
   void* O;                        // [M,H]
   // backward intermediates / outputs (fp32 in fp8_bwd mode)

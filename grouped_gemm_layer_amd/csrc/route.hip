@@ -33,20 +33,17 @@ __device__ __forceinline__ void best_dpp(float& bv, int& be) {
   const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
   take_better(ov, oe, bv, be);
 }
-// the gfx950 row swaps pair rows 0-1 and 2-3 (16) or halves (32); each lane
-// gets its own and its partner's value, in the same order for both words
-__device__ __forceinline__ void best_swap16(float& bv, int& be) {
-  const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-  const auto re = __builtin_amdgcn_permlane16_swap((uint32_t)be, (uint32_t)be, false, false);
-  float v = __uint_as_float(rv[0]);
-  int e = (int)re[0];
-  take_better(__uint_as_float(rv[1]), (int)re[1], v, e);
-  bv = v;
-  be = e;
-}
-__device__ __forceinline__ void best_swap32(float& bv, int& be) {
-  const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-  const auto re = __builtin_amdgcn_permlane32_swap((uint32_t)be, (uint32_t)be, false, false);
+// one cross-lane step through a gfx950 row swap (rows 0-1 and 2-3 for 16,
+// the two halves for 32): the swap returns each lane its own and its
+// partner's word, in the same order for the value and the expert
+template <int ROWS>
+__device__ __forceinline__ void best_swap(float& bv, int& be) {
+  const auto swap = [](uint32_t w) {
+    if constexpr (ROWS == 16) return __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    else return __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  };
+  const auto rv = swap(__float_as_uint(bv));
+  const auto re = swap((uint32_t)be);
   float v = __uint_as_float(rv[0]);
   int e = (int)re[0];
   take_better(__uint_as_float(rv[1]), (int)re[1], v, e);
@@ -87,8 +84,8 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     best_dpp<0x4E>(bv, be);    // quad_perm 2,3,0,1
     best_dpp<0x141>(bv, be);   // row_half_mirror
     best_dpp<0x140>(bv, be);   // row_mirror
-    best_swap16(bv, be);
-    best_swap32(bv, be);
+    best_swap<16>(bv, be);
+    best_swap<32>(bv, be);
     if (lane == (be & 63)) live &= ~(1u << (be >> 6));
     if (j == 0) v0 = bv;
     if (lane == j) { my_v = bv; my_e = be; }
