@@ -128,7 +128,15 @@ def test_forward_backward_argument_errors():
         g.backward(d, t(0), t(1), t(2), t(3), r, t(4), t(5), t(6), t(7), t(8), None,
                    _FakeTensor(0x7B0000000000, 1), stream=_NullStream(), accumulate=True)
     assert ei.value.status == 5
-    # the checkpointing recompute has moe_forward's checks, without y
+    # saved may be NULL for moe_forward (nothing kept for a backward): the
+    # call gets past the pointer checks to the workspace check
+    with pytest.raises(g.MoeError) as ei:
+        g.forward(d, t(0), t(1), t(2), r, t(3), None, _FakeTensor(0x7B0000000000, 255), stream=_NullStream())
+    assert ei.value.status == 5
+    # the checkpointing recompute has moe_forward's checks, without y, and needs saved
+    with pytest.raises(g.MoeError) as ei:
+        g.forward_recompute(d, t(0), t(1), t(2), r, None, t(5), stream=_NullStream())
+    assert ei.value.status == 1
     with pytest.raises(g.MoeError) as ei:
         g.forward_recompute(d, t(0), t(1), None, r, t(4), t(5), stream=_NullStream())
     assert ei.value.status == 1
