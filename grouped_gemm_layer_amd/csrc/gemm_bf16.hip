@@ -423,14 +423,16 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   gg::gemm_epilogue<KIND, C>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout, wacc);
 }
 
-// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile).
-// Forward: 256 x 256 tiles with a 64-wide K tile (128-byte rows per DMA
-// lane group, one 8-wave block per CU): fewer operand bytes per flop and full
-// cache lines outweigh the longer ragged tail (measured 8 % faster for both
-// forward GEMMs).  The dgrad kinds measured faster with 128 x 256, K tile 32,
-// two 4-wave blocks per CU.
+// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile,
+// tile-group divisor).  Forward: 256 x 256 tiles with a 64-wide K tile
+// (128-byte rows per DMA lane group, one 8-wave block per CU): fewer operand
+// bytes per flop and full cache lines outweigh the longer ragged tail
+// (measured 8 % faster for both forward GEMMs); tile groups of 8 blocks, a
+// quarter of an XCD's resident blocks (about 2 % faster than 32).  The dgrad
+// kinds measured faster with 128 x 256, K tile 32, two 4-wave blocks per CU,
+// and whole-XCD tile groups.
 #ifndef MOE_CFG_ROW_FWD
-#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64
+#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64, 4
 #endif
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32

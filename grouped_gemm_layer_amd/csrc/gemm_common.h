@@ -60,7 +60,7 @@ __device__ __forceinline__ bool decode_row_tile(const LayerArgs& a, int L, int n
   return true;
 }
 
-template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64>
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64, int GD_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
   static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
@@ -71,8 +71,9 @@ struct TileCfg {
   // 1 KiB LDS DMA instructions per wave per K tile, A and B operands
   // (bf16 operands: BK elements = 2*BK bytes per row)
   static constexpr int DA = BM * BK * 2 / 1024 / NW, DB = BN * BK * 2 / 1024 / NW;
-  // blocks resident on one XCD at a time: the size of the tile groups that share operands
-  static constexpr int GROUP = 32 * (4 * WPE) / NW;
+  // tile groups that share operands: blocks resident on one XCD at a time,
+  // divided by GD (smaller groups measured faster for the forward kinds)
+  static constexpr int GROUP = 32 * (4 * WPE) / NW / GD_;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(DA * NW * 1024 == BM * BK * 2 && DB * NW * 1024 == BN * BK * 2, "tiles must split into 1 KiB DMA rows");
   static constexpr int SMEM_BYTES = STAGES * (BM + BN) * BK * 2;   // operand LDS of the kernel
