@@ -68,8 +68,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows
 template <typename T>
 hipError_t launch_combine(const T* rows, const int32_t* f2s, const float* gate, int Tn, int k, int H, T* out,
                           hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel<T>, dim3(Tn), dim3(256), 0, s, rows, f2s, gate, k, H, out);
-  return hipGetLastError();
+  return launch_kernel(combine_kernel<T>, dim3(Tn), dim3(256), 0, s, rows, f2s, gate, k, H, out);
 }
 template hipError_t launch_combine<bf16_t>(const bf16_t*, const int32_t*, const float*, int, int, int, bf16_t*,
                                            hipStream_t);
@@ -126,9 +125,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 hipError_t launch_router_bwd(const float* dgate_part, int n_parts, const int32_t* f2s, const float* gate,
                              const int32_t* topk_idx, int Tn, int k, int E, int M, float* dgate, float* dlogits,
                              hipStream_t s) {
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((Tn + 3) / 4), dim3(256), 0, s, dgate_part, n_parts, f2s, gate,
+  return launch_kernel(router_bwd_kernel, dim3((Tn + 3) / 4), dim3(256), 0, s, dgate_part, n_parts, f2s, gate,
                      topk_idx, Tn, k, E, M, dgate, dlogits);
-  return hipGetLastError();
 }
 
 // Split-K completion of the weight gradients: for each expert whose rows were
@@ -177,9 +175,8 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int32_t* __rest
 hipError_t launch_wgrad_reduce(const LayerArgs& a, hipStream_t s) {
   const int ranks = max(1, min(a.E, (int)wgrad_max_slots((size_t)a.M)));   // split experts come first
   const size_t n13 = (size_t)2 * a.I * a.H, n2 = (size_t)a.H * a.I;
-  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(512, ranks, 2), dim3(256), 0, s, a.wg_order, a.wg_cstart,
+  return launch_kernel(wgrad_reduce_kernel, dim3(512, ranks, 2), dim3(256), 0, s, a.wg_order, a.wg_cstart,
                      a.wg_slot0, a.dw13, a.wpart13, n13, a.dw2, a.wpart2, n2);
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -460,8 +460,7 @@ hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
   }
   const int grid = Kind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
                                            : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
-  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, n_tiles, tiles);
-  return hipGetLastError();
+  return launch_kernel((gemm_bf16_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, n_tiles, tiles);
 }
 
 }  // namespace

@@ -178,36 +178,30 @@ hipError_t launch_gemm_fp32(GemmKind kind, const LayerArgs& a, hipStream_t s) {
   switch (kind) {
     case KIND_FWD1: {
       const int nt = (a.I + BN / 2 - 1) / (BN / 2);
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_FWD1>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_FWD1>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
     }
     case KIND_FWD2: {
       const int nt = (a.H + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_FWD2>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_FWD2>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
     }
     case KIND_DGRAD2: {
       const int nt = (a.I + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_DGRAD2>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_DGRAD2>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
     }
     case KIND_DGRAD1: {
       const int nt = (a.H + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_DGRAD1>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_DGRAD1>, dim3(nt * max_mt), dim3(256), 0, s, a, nt);
     }
     case KIND_WGRAD2: {
       const int nt = (a.I + BN - 1) / BN, mt = (a.H + BM - 1) / BM;
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_WGRAD2>, dim3(nt * mt, a.E), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_WGRAD2>, dim3(nt * mt, a.E), dim3(256), 0, s, a, nt);
     }
     case KIND_WGRAD1: {
       const int nt = (a.H + BN - 1) / BN, mt = (2 * a.I + BM - 1) / BM;
-      hipLaunchKernelGGL(gemm_fp32_kernel<KIND_WGRAD1>, dim3(nt * mt, a.E), dim3(256), 0, s, a, nt);
-      break;
+      return launch_kernel(gemm_fp32_kernel<KIND_WGRAD1>, dim3(nt * mt, a.E), dim3(256), 0, s, a, nt);
     }
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

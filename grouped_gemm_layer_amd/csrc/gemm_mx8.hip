@@ -329,8 +329,7 @@ hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
   }
   const int grid = MxKind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
                                              : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
-  hipLaunchKernelGGL((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles);
-  return hipGetLastError();
+  return launch_kernel((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles);
 }
 
 }  // namespace

@@ -6,6 +6,10 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -133,7 +137,26 @@ enum GemmKind {
 };
 
 // ---------------------------------------------------------------------------
-// Launchers (each returns hipGetLastError() of its launch).
+// Kernel launch through hipLaunchKernel: returns the status of this launch
+// itself, never an error left behind by an earlier, unrelated HIP call (and
+// leaves the caller's last-error state alone when the launch succeeds).
+// ---------------------------------------------------------------------------
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                                A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<std::remove_cv_t<std::remove_reference_t<P>>...> vals(std::forward<A>(args)...);
+  return std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {const_cast<void*>(static_cast<const void*>(&v))...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, s);
+      },
+      vals);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns the status of its own launches; a launcher with
+// several kernels stops at the first failure).
 // ---------------------------------------------------------------------------
 // routing
 // router projection (router.hip): logits = x W_r^T; backward: dx += dlogits W_r, dW_r = dlogits^T x

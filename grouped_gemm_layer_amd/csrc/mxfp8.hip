@@ -252,8 +252,7 @@ hipError_t launch_mx_quant_rows(const T* src, int R, int K, const int32_t* s2f, 
                                 uint8_t* scales, hipStream_t s) {
   const long total = (long)R * (K / 32);
   const int grid = (int)min((total + 255) / 256, (long)65536);
-  hipLaunchKernelGGL(mx_quant_rows_kernel<T>, dim3(grid), dim3(256), 0, s, src, R, K, s2f, k, codes, scales);
-  return hipGetLastError();
+  return launch_kernel(mx_quant_rows_kernel<T>, dim3(grid), dim3(256), 0, s, src, R, K, s2f, k, codes, scales);
 }
 template hipError_t launch_mx_quant_rows<bf16_t>(const bf16_t*, int, int, const int32_t*, int, uint8_t*, uint8_t*,
                                                  hipStream_t);
@@ -266,31 +265,27 @@ inline int qt_grid(int F, int np, int ne) {
 
 hipError_t launch_mx_quant_cols_t(const bf16_t* src, int E, int Kd, int N, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s) {
-  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s, src,
-                     N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes, scales, Kd / MX_KTILE, E);
-  return hipGetLastError();
+  return launch_kernel((mx_quant_t_kernel<bf16_t, false>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s, src,
+                     N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes, scales, Kd / MX_KTILE, E, nullptr, nullptr);
 }
 
 hipError_t launch_mx_quant_both(const bf16_t* src, int E, int Kd, int N, uint8_t* codes_t, uint8_t* scales_t,
                                 uint8_t* codes_r, uint8_t* scales_r, hipStream_t s) {
-  hipLaunchKernelGGL((mx_quant_t_kernel<bf16_t, false, true>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s,
+  return launch_kernel((mx_quant_t_kernel<bf16_t, false, true>), dim3(qt_grid(N, Kd / MX_KTILE, E)), dim3(256), 0, s,
                      src, N, nullptr, 1, nullptr, nullptr, E, Kd, Kd, codes_t, scales_t, Kd / MX_KTILE, E, codes_r,
                      scales_r);
-  return hipGetLastError();
 }
 
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t s) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(512), 0, s, offsets, E, pad_off);
-  return hipGetLastError();
+  return launch_kernel(pad_offsets_kernel, dim3(1), dim3(512), 0, s, offsets, E, pad_off);
 }
 
 template <typename T>
 hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int k, const int32_t* offsets,
                                     const int32_t* pad_off, int E, int Mp, uint8_t* codes, uint8_t* scales,
                                     hipStream_t s) {
-  hipLaunchKernelGGL((mx_quant_t_kernel<T, true>), dim3(qt_grid(F, Mp / MX_KTILE, 1)), dim3(256), 0, s, src, F, s2f,
-                     k, offsets, pad_off, E, 0, Mp, codes, scales, Mp / MX_KTILE, 1);
-  return hipGetLastError();
+  return launch_kernel((mx_quant_t_kernel<T, true>), dim3(qt_grid(F, Mp / MX_KTILE, 1)), dim3(256), 0, s, src, F, s2f,
+                     k, offsets, pad_off, E, 0, Mp, codes, scales, Mp / MX_KTILE, 1, nullptr, nullptr);
 }
 template hipError_t launch_mx_quant_tokens_t<bf16_t>(const bf16_t*, int, const int32_t*, int, const int32_t*,
                                                      const int32_t*, int, int, uint8_t*, uint8_t*, hipStream_t);

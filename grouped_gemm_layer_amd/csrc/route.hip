@@ -13,6 +13,7 @@
 
 #include <math.h>
 
+
 namespace moe {
 
 constexpr int ROUTE_CHUNK = 4096;   // flat slots per block of the histogram / scatter
@@ -222,13 +223,16 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
   const int nblk = route_num_blocks(M);
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
-  hipLaunchKernelGGL(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, gate);
-  hipLaunchKernelGGL(expert_hist_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, M, E, ws_partials);
-  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, ws_partials, nblk, E, ws_bases,
-                     counts, offsets);
-  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, M, E, ebits, ws_bases,
-                     s2f, f2s);
-  return hipGetLastError();
+  hipError_t e = launch_kernel(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, gate);
+  if (e == hipSuccess)
+    e = launch_kernel(expert_hist_kernel, dim3(nblk), dim3(256), 0, s, (const int32_t*)topk_idx, M, E, ws_partials);
+  if (e == hipSuccess)
+    e = launch_kernel(expert_scan_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)ws_partials, nblk, E, ws_bases,
+                      counts, offsets);
+  if (e == hipSuccess)
+    e = launch_kernel(expert_scatter_kernel, dim3(nblk), dim3(256), 0, s, (const int32_t*)topk_idx, M, E, ebits,
+                      (const int32_t*)ws_bases, s2f, f2s);
+  return e;
 }
 
 // Tile table of the row-ragged GEMMs: tile i covers rows [row0, row0 + bm) of
@@ -318,9 +322,8 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles, int32_t* tile_expert,
                              int32_t* tile_row0, int32_t* expert_tile0, WgradList wg, hipStream_t s) {
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
-                     tile_row0, expert_tile0, wg);
-  return hipGetLastError();
+  return launch_kernel(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, max_tiles, tile_expert,
+                       tile_row0, expert_tile0, wg);
 }
 
 }  // namespace moe

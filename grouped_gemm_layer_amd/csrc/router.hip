@@ -200,20 +200,17 @@ __global__ __launch_bounds__(64 * RDW_NW) void router_dw_kernel(const float* __r
 
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* wr, int T, int H, int E, float* logits,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(router_logits_kernel, dim3((T + RL_T - 1) / RL_T, (E + RL_E - 1) / RL_E), dim3(64 * RL_NW), 0, s, x,
-                     wr, T, H, E, logits);
-  return hipGetLastError();
+  return launch_kernel(router_logits_kernel, dim3((T + RL_T - 1) / RL_T, (E + RL_E - 1) / RL_E), dim3(64 * RL_NW), 0,
+                       s, x, wr, T, H, E, logits);
 }
 
 hipError_t launch_router_project_bwd(const float* dlogits, const int32_t* topk_idx, const int32_t* offsets,
                                      const int32_t* s2f, const bf16_t* x, const bf16_t* wr, int T, int H, int E,
                                      int k, bf16_t* dx, float* dwr, hipStream_t s) {
-  hipLaunchKernelGGL(router_dx_kernel, dim3(T), dim3(256), 0, s, dlogits, topk_idx, wr, k, H, E, dx);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(router_dx_kernel, dim3(T), dim3(256), 0, s, dlogits, topk_idx, wr, k, H, E, dx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_dw_kernel, dim3((H + RDW_COLS - 1) / RDW_COLS, E), dim3(64 * RDW_NW), 0, s, dlogits, offsets,
-                     s2f, x, k, H, E, dwr);
-  return hipGetLastError();
+  return launch_kernel(router_dw_kernel, dim3((H + RDW_COLS - 1) / RDW_COLS, E), dim3(64 * RDW_NW), 0, s, dlogits,
+                       offsets, s2f, x, k, H, E, dwr);
 }
 
 }  // namespace moe

@@ -25,8 +25,14 @@
  *     global state; calls with distinct workspaces may run concurrently.
  *   - Every call only enqueues work on `stream` (no host synchronisation, no
  *     device-to-host copy), so a call may be captured in a HIP graph.
- *   - Validation happens on the host before any launch.  A non-zero status
- *     means nothing was enqueued.  Launch errors map to MOE_ERR_LAUNCH.
+ *   - Validation happens on the host before any launch: every status other
+ *     than MOE_OK and MOE_ERR_LAUNCH means nothing was enqueued.
+ *   - MOE_ERR_LAUNCH is the failure of one of the call's own kernel launches
+ *     (the status hipLaunchKernel returned for it; an error left behind by an
+ *     earlier, unrelated HIP call is neither reported nor cleared).  A call
+ *     launches its kernels in order and stops at the first failure, so the
+ *     kernels before it may already be enqueued: the outputs are then
+ *     undefined, and the workspace and `saved` contents too.
  *   - Device pointers must be 256-byte aligned; buffers may not alias.
  *   - Results are deterministic: bitwise identical for identical inputs.
  *
@@ -38,8 +44,10 @@
  * patterns) otherwise.  Gates, gate/logit gradients and weight gradients are
  * always fp32.  Current limits: H and I multiples of 64 (H a multiple of 128
  * in MOE_MODE_FP8_BWD, H and I multiples of 128 in MOE_MODE_MXFP8), E <= 512,
- * k <= 32, and every activation-sized buffer below 2 GiB (MOE_ERR_UNSUPPORTED
- * otherwise).
+ * k <= 32, and every activation-sized buffer below 2 GiB (the kernels address
+ * each operand through 32-bit byte offsets; e.g. T = 32768 at H = 4096 needs
+ * M*H*2 = 2 GiB for the permuted rows and is rejected): MOE_ERR_UNSUPPORTED
+ * otherwise.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -66,7 +74,7 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 3,  /* valid but outside this build's limits (mode, H/I % 64, E, k) */
   MOE_ERR_ALIGN = 4,        /* a device pointer is not 256-byte aligned */
   MOE_ERR_WORKSPACE = 5,    /* workspace smaller than moe_workspace_size reports */
-  MOE_ERR_LAUNCH = 6        /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_LAUNCH = 6        /* a kernel launch of the call failed; earlier kernels may be enqueued */
 } moe_status;
 
 typedef struct {

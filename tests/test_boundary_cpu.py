@@ -248,3 +248,22 @@ def test_router_projection_argument_errors():
         g.router_backward(g.Dims.of(64, 128, 64, 8, 2, "fp32"), r, t(0), t(1), t(2), t(3), t(4),
                           stream=_NullStream())
     assert ei.value.status == 3
+
+
+def test_launch_status_is_the_launch_own():
+    """A call that passes validation reaches its first launch; the status it
+    returns is that launch's own.  On a machine without a GPU the launch fails
+    and the call reports MOE_ERR_LAUNCH, while invalid arguments still return
+    their validation status first (nothing is launched)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("checks the launch failure of a machine without a GPU")
+    g, lib = _lib()
+    d = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    r = _fake_routing(g)
+    c = r.c()
+    logits, ws = 0x7E0000000000, 0x7D0000000000
+    assert lib.moe_route(ctypes.byref(d), ctypes.c_void_p(logits), ctypes.byref(c), ctypes.c_void_p(ws), 16,
+                         None) == 5
+    assert lib.moe_route(ctypes.byref(d), ctypes.c_void_p(logits), ctypes.byref(c), ctypes.c_void_p(ws), 1 << 20,
+                         None) == 6

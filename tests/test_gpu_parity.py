@@ -183,3 +183,22 @@ def test_route_extremes_exact(T, E, k, ties, seed):
     run = GpuRun(d, inp)
     run.route()
     check_routing_exact(run.routing_np(), orc.route(inp["logits"], d.k))
+
+
+def test_leftover_error_not_blamed_on_the_library():
+    """An error left by an earlier, unrelated HIP call (an invalid device id)
+    is neither reported by a valid library call nor cleared by it: the
+    library reports the status of its own launches."""
+    import ctypes
+    import torch
+    d = mi.LayerDims(T=256, H=128, I=64, E=8, k=2, dtype="bf16")
+    inp = mi.make_inputs(d, 130)
+    run = GpuRun(d, inp)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipGetLastError()                               # start from a clean state
+    assert hip.hipSetDevice(100000) != 0                # leaves an error behind
+    run.route()                                          # raises unless the call returns MOE_OK
+    torch.cuda.synchronize()
+    assert hip.hipGetLastError() != 0                    # still there for its owner
+    assert hip.hipGetLastError() == 0
+    check_routing_exact(run.routing_np(), orc.route(inp["logits"], d.k))
