@@ -7,6 +7,7 @@ binding raises if the built library is missing; there is no fallback.
 Names follow the C ABI in include/moe.h:
     workspace_size(dims) -> (route_ws, saved, fwd_ws, bwd_ws)
     route(dims, logits, routing, ws)
+    route_noalloc(dims, logits, routing)
     forward(dims, x, w13, w2, routing, y, saved, ws)
     backward(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws)
     mxfp8_quantize(src, along, codes, scales)
@@ -23,7 +24,7 @@ __all__ = [
     "MODE_FP32", "MODE_BF16", "MODE_MXFP8", "MODE_FP8_BWD", "Dims", "RoutingBuffers",
     "MoeError", "lib_path", "load_library", "workspace_size", "route", "forward", "backward",
     "alloc_routing", "alloc_workspace", "status_str", "MoeLayer", "num_kernels", "mxfp8_quantize",
-    "mxfp8_quantize_grouped", "mxfp8_grouped_capacity",
+    "mxfp8_quantize_grouped", "mxfp8_grouped_capacity", "route_noalloc",
 ]
 
 MODE_FP32, MODE_BF16, MODE_MXFP8, MODE_FP8_BWD = 0, 1, 2, 3
@@ -85,6 +86,8 @@ def load_library():
                                  vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_workspace_size", "moe_route", "moe_forward", "moe_backward"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.moe_route_noalloc.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(_CRouting), vp]
+    lib.moe_route_noalloc.restype = ctypes.c_int
     lib.moe_route_project.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, ctypes.POINTER(_CRouting), vp, sz, vp]
     lib.moe_route_project.restype = ctypes.c_int
     lib.moe_router_backward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_CRouting), vp, vp, vp, vp, vp, vp]
@@ -171,6 +174,15 @@ def route(dims: Dims, logits, routing: RoutingBuffers, ws, stream=None):
     r = routing.c()
     _check(lib.moe_route(ctypes.byref(dims), _ptr(logits), ctypes.byref(r), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_route")
+
+
+def route_noalloc(dims: Dims, logits, routing: RoutingBuffers, stream=None):
+    """moe_route_noalloc: routing without a workspace (the library's static
+    per-device scratch; calls that overlap on one GPU race)."""
+    lib = load_library()
+    r = routing.c()
+    _check(lib.moe_route_noalloc(ctypes.byref(dims), _ptr(logits), ctypes.byref(r), _stream(stream)),
+           "moe_route_noalloc")
 
 
 def route_project(dims: Dims, x, w_router, logits, routing: RoutingBuffers, ws, stream=None):

@@ -254,6 +254,25 @@ moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routin
   return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+moe_status moe_route_noalloc(const moe_dims* dims, const float* logits, const moe_routing* out,
+                             hipStream_t stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(out)) != MOE_OK) return st;
+  if (!logits) return MOE_ERR_NULL;
+  if (!aligned(logits)) return MOE_ERR_ALIGN;
+  const Sizes s = compute_sizes(dims);
+  static_assert(MOE_ROUTE_NOALLOC_MAX_BYTES == ROUTE_SCRATCH_BYTES, "header and library agree on the scratch size");
+  if (s.route_ws > ROUTE_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;   // this device's address of the library's routing scratch
+  if (route_scratch_ptr(&ws) != hipSuccess) return MOE_ERR_LAUNCH;
+  const hipError_t e = launch_route(logits, dims->T, dims->E, dims->k, out->topk_idx, out->gate, out->counts,
+                                    out->offsets, out->sorted_to_flat, out->flat_to_sorted,
+                                    reinterpret_cast<int32_t*>(at(ws, s.r_partials)),
+                                    reinterpret_cast<int32_t*>(at(ws, s.r_bases)), stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 moe_status moe_route_project(const moe_dims* dims, const void* x, const void* w_router, float* logits,
                              const moe_routing* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_dims(dims);

@@ -169,6 +169,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
                         int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
                         int32_t* ws_partials, int32_t* ws_bases, hipStream_t s);
 int route_num_blocks(int M);   // blocks of the histogram / scatter passes
+// Library-held routing scratch of moe_route_noalloc (a static device array,
+// one per GPU): its size, and this device's address of it (looked up once per
+// device, on the first call with that device current).
+constexpr size_t ROUTE_SCRATCH_BYTES = (size_t)2 << 20;
+hipError_t route_scratch_ptr(void** ptr);
 
 // Rows per weight-gradient chunk: an expert with more rows is split along K
 // (its rows) into chunks of WG_KC rows (a multiple of the 128-row MXFP8 K tile

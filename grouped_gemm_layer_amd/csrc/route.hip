@@ -13,6 +13,7 @@
 
 #include <math.h>
 
+#include <mutex>
 
 namespace moe {
 
@@ -214,6 +215,33 @@ __global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* __re
     }
     __syncthreads();
   }
+}
+
+// Routing scratch of the allocation-free entry point: the per-block expert
+// partials and block bases (2 * blocks * E int32), in a file-scope device
+// array that every GPU the library runs on holds until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// is only a stand-in for the symbol); it takes each device's address of the
+// array from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[ROUTE_SCRATCH_BYTES];
+
+hipError_t route_scratch_ptr(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* gate,

@@ -22,7 +22,8 @@
  *   - Every pointer argument named as "device" is a device pointer; dims and
  *     routing structs are host pointers read during the call only.
  *   - The caller owns all memory.  The library allocates nothing and keeps no
- *     global state; calls with distinct workspaces may run concurrently.
+ *     global state, apart from the static routing scratch of
+ *     moe_route_noalloc; calls with distinct workspaces may run concurrently.
  *   - Every call only enqueues work on `stream` (no host synchronisation, no
  *     device-to-host copy), so a call may be captured in a HIP graph.
  *   - Validation happens on the host before any launch: every status other
@@ -111,6 +112,23 @@ moe_status moe_workspace_size(const moe_dims* dims, size_t* route_ws, size_t* sa
  * deterministic.  logits: device [T,E] fp32, finite values. */
 moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_route without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same results, bit for bit, and the same
+ * arguments otherwise.  The per-block expert partials and bases live in a
+ * static device array of MOE_ROUTE_NOALLOC_MAX_BYTES that the library holds
+ * on every GPU it runs on until the process ends (its address is looked up
+ * on the first call on each device); the call allocates nothing.  Shapes
+ * whose routing workspace (moe_workspace_size's route_ws, 2 * ceil(T*k /
+ * 4096) * E * 4 bytes rounded up to 256) exceeds it return MOE_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in the array needs clearing: each call writes every entry
+ * it reads. */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES ((size_t)2 << 20)
+moe_status moe_route_noalloc(const moe_dims* dims, const float* logits, const moe_routing* out,
+                             hipStream_t stream);
 
 /* Router projection, then moe_route (TE dropless-MoE page, "01 Why is MoE
  * training harder than dense training?": the router is a trained component):

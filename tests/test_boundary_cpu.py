@@ -267,3 +267,20 @@ def test_launch_status_is_the_launch_own():
                          None) == 5
     assert lib.moe_route(ctypes.byref(d), ctypes.c_void_p(logits), ctypes.byref(c), ctypes.c_void_p(ws), 1 << 20,
                          None) == 6
+
+
+def test_route_noalloc_limit_checked_before_launch():
+    """moe_route_noalloc validates like moe_route and rejects shapes whose
+    routing scratch exceeds the library's static array before any launch."""
+    g, lib = _lib()
+    r = _fake_routing(g)
+    c = r.c()
+    logits = ctypes.c_void_p(0x7E0000000000)
+    big = g.Dims.of(131072, 64, 64, 512, 32, "bf16")          # 4 MiB of block partials
+    assert g.workspace_size(big)[0] > 2 << 20
+    assert lib.moe_route_noalloc(ctypes.byref(big), logits, ctypes.byref(c), None) == 5
+    ok = g.Dims.of(64, 128, 64, 8, 2, "bf16")
+    assert lib.moe_route_noalloc(ctypes.byref(ok), None, ctypes.byref(c), None) == 1
+    assert lib.moe_route_noalloc(ctypes.byref(ok), ctypes.c_void_p(0x7E0000000004), ctypes.byref(c), None) == 4
+    assert lib.moe_route_noalloc(ctypes.byref(g.Dims.of(64, 128, 64, 8, 9, "bf16")), logits, ctypes.byref(c),
+                                 None) == 2
