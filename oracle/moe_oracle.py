@@ -67,7 +67,7 @@ import numpy as np
 __all__ = [
     "Routing", "route", "silu", "sigmoid", "expert_forward", "expert_backward",
     "forward", "backward", "router_backward", "forward_with_gates",
-    "e4m3fn_decode_table", "e4m3fn_encode", "mx_scale_exponent", "mx_quant_dequant",
+    "e4m3fn_decode_table", "e4m3fn_encode", "e4m3fn_round", "mx_scale_exponent", "mx_quant_dequant", "mx_dequant",
     "mx_quant_dequant_tokens", "expert_backward_mxfp8", "backward_mxfp8", "expert_forward_mxfp8",
     "forward_mxfp8",
 ]
@@ -314,6 +314,27 @@ def e4m3fn_encode(v: np.ndarray) -> np.ndarray:
     return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
+def e4m3fn_round(v: np.ndarray) -> np.ndarray:
+    """Value of e4m3fn_encode(v) (float64, sign kept also for zero), computed
+    without building codes.
+
+    Inside a binade [2**e, 2**(e+1)) with e >= -6 the E4M3FN magnitudes are
+    the multiples of 2**(e-3) (mantissa 1.mmm); below 2**-6 (the subnormals)
+    they are the multiples of 2**-9.  Consecutive codes are consecutive
+    multiples and a code's last mantissa bit is the parity of its multiple, so
+    rounding |v| to the nearest multiple of its binade's step with ties to the
+    even multiple (numpy's round) is rounding to the nearest code with ties to
+    the even code; |v| is first clipped to 448 (saturation), itself a multiple
+    of its step.  frexp gives the binade exactly; every scaling is by a power
+    of two, hence exact."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    _, ex = np.frexp(a)                         # a = m * 2**ex, m in [0.5, 1): binade e = ex - 1
+    step_exp = np.maximum(ex - 1, -6) - 3
+    r = np.ldexp(np.round(np.ldexp(a, -step_exp)), step_exp)
+    return np.copysign(r, v)
+
+
 def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
     """Smallest integer X in [-127, 127] with amax <= 448 * 2**X (amax = 0 -> -127).
 
@@ -348,6 +369,20 @@ def mx_quant_dequant(a: np.ndarray, axis: int = -1):
     return deq, codes, X
 
 
+def mx_dequant(a: np.ndarray, axis: int = -1) -> np.ndarray:
+    """dequant(quant(a)) along `axis` in blocks of 32: the first value
+    mx_quant_dequant returns, with the elements rounded by e4m3fn_round (the
+    same values, without the codes)."""
+    a = np.asarray(a, dtype=np.float64)
+    a_m = np.moveaxis(a, axis, -1)
+    n = a_m.shape[-1]
+    assert n % 32 == 0
+    blk = a_m.reshape(a_m.shape[:-1] + (n // 32, 32))
+    X = mx_scale_exponent(np.max(np.abs(blk), axis=-1))[..., None]
+    deq = np.ldexp(e4m3fn_round(np.ldexp(blk, -X)), X)
+    return np.moveaxis(deq.reshape(a_m.shape), -1, axis)
+
+
 def mx_quant_dequant_tokens(a: np.ndarray, offsets: np.ndarray) -> np.ndarray:
     """Group-aware quantisation along the row (token) axis of a [M, N] array:
     32-row blocks start at each expert's first row; the tail is zero-padded."""
@@ -361,8 +396,7 @@ def mx_quant_dequant_tokens(a: np.ndarray, offsets: np.ndarray) -> np.ndarray:
         npad = (n + 31) // 32 * 32
         seg = np.zeros((npad, a.shape[1]))
         seg[:n] = a[lo:hi]
-        deq, _, _ = mx_quant_dequant(seg, axis=0)
-        out[lo:hi] = deq[:n]
+        out[lo:hi] = mx_dequant(seg, axis=0)[:n]
     return out
 
 
@@ -384,16 +418,16 @@ def expert_backward_mxfp8(dYp, Xp, g, w13e, w2e, fwd: dict) -> dict:
     Xp = np.asarray(Xp, dtype=np.float64)
     n = dYp.shape[0]
     seg = np.array([0, n])
-    qW2, _, _ = mx_quant_dequant(np.asarray(w2e, dtype=np.float64), axis=0)      # [H, I], K = H
-    qdYp, _, _ = mx_quant_dequant(dYp, axis=1)
+    qW2 = mx_dequant(np.asarray(w2e, dtype=np.float64), axis=0)      # [H, I], K = H
+    qdYp = mx_dequant(dYp, axis=1)
     dAp = qdYp @ qW2
     A, G1, G3 = fwd["A"], fwd["G1"], fwd["G3"]
     dgate = np.sum(dAp * A, axis=1)
     dA = g[:, None] * dAp
     s = sigmoid(G1)
     dG = np.concatenate([dA * G3 * s * (1.0 + G1 * (1.0 - s)), dA * G1 * s], axis=1)
-    qW13, _, _ = mx_quant_dequant(np.asarray(w13e, dtype=np.float64), axis=0)   # [2I, H], K = 2I
-    qdG, _, _ = mx_quant_dequant(dG, axis=1)
+    qW13 = mx_dequant(np.asarray(w13e, dtype=np.float64), axis=0)   # [2I, H], K = 2I
+    qdG = mx_dequant(dG, axis=1)
     dXp = qdG @ qW13
     dW2 = mx_quant_dequant_tokens(dYp, seg).T @ mx_quant_dequant_tokens(g[:, None] * A, seg)
     dW13 = mx_quant_dequant_tokens(dG, seg).T @ mx_quant_dequant_tokens(Xp, seg)
@@ -439,10 +473,10 @@ def expert_forward_mxfp8(xrows, w13e, w2e) -> dict:
     W13 = np.asarray(w13e, dtype=np.float64)
     W2 = np.asarray(w2e, dtype=np.float64)
     I = W13.shape[0] // 2
-    G = mx_quant_dequant(X, axis=1)[0] @ mx_quant_dequant(W13, axis=1)[0].T
+    G = mx_dequant(X, axis=1) @ mx_dequant(W13, axis=1).T
     G1, G3 = G[:, :I], G[:, I:]
     A = silu(G1) * G3
-    O = mx_quant_dequant(A, axis=1)[0] @ mx_quant_dequant(W2, axis=1)[0].T
+    O = mx_dequant(A, axis=1) @ mx_dequant(W2, axis=1).T
     return {"G1": G1, "G3": G3, "A": A, "O": O}
 
 

@@ -48,6 +48,38 @@ def test_round_half_to_even_midpoints():
     assert enc.tolist() == [0x38, 0x3A, 0x00, 0x02, 0xB8, 0x7E, 0x7E, 0xFE]
 
 
+def test_round_equals_decoded_encoding():
+    """e4m3fn_round (the value, computed from the binade's step) equals the
+    decoded code of e4m3fn_encode (nearest of the 127 table values, ties to the
+    even code) on every code value, every midpoint between neighbours (and one
+    ulp either side), random values over all binades, subnormals, saturation
+    and signed zeros."""
+    tab = orc.e4m3fn_decode_table()
+    pos = tab[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2.0
+    rng = np.random.default_rng(12)
+    v = np.concatenate([pos, mids, np.nextafter(mids, 0.0), np.nextafter(mids, 1e9),
+                        np.exp2(rng.uniform(-14, 10, 50000)), rng.uniform(0, 2.0 ** -6, 5000),
+                        [0.0, 448.0, 449.0, 464.0, 479.99, 480.0, 1e9, 2.0 ** -10, 2.0 ** -11]])
+    v = np.concatenate([v, -v])
+    ref = np.copysign(tab[orc.e4m3fn_encode(v) & 0x7F], v)
+    got = orc.e4m3fn_round(v)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(v))
+
+
+def test_dequant_equals_quant_dequant():
+    rng = np.random.default_rng(13)
+    a = rng.standard_normal((48, 256)) * np.exp(rng.uniform(-30, 30, (48, 1)))
+    a[0, :32] = 0.0
+    a[1, :32] = -0.0
+    a[2, 32:64] = 1.0625 * 2.0 ** np.arange(-16, 16)
+    for axis in (0, 1):
+        b = a if axis == 1 else a[:, :96].T.copy()
+        deq, _, _ = orc.mx_quant_dequant(b, axis=axis)
+        assert np.array_equal(orc.mx_dequant(b, axis=axis), deq)
+
+
 def test_scale_rule():
     amax = np.array([448.0, 448.00001, 224.0, 224.0001, 1.0, 0.0, 3.5, 1e-30, 2.0 ** 130])
     X = orc.mx_scale_exponent(amax)
@@ -113,7 +145,7 @@ def test_quantised_backward_structure_with_identity_quantiser(monkeypatch):
     r = orc.route(inp["logits"], d.k)
     Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
     g = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
-    monkeypatch.setattr(orc, "mx_quant_dequant", lambda a, axis=-1: (np.asarray(a, np.float64), None, None))
+    monkeypatch.setattr(orc, "mx_dequant", lambda a, axis=-1: np.asarray(a, np.float64))
     monkeypatch.setattr(orc, "mx_quant_dequant_tokens", lambda a, offsets: np.asarray(a, np.float64))
     q = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
     for key in ("dx", "dw13", "dw2", "dgate", "dlogits"):
@@ -137,14 +169,14 @@ def test_quantised_operands_are_blocked_along_each_gemms_k(monkeypatch):
     def rec(a, axis=-1):
         a = np.asarray(a, np.float64)
         calls.append(("rows", a.shape, axis % a.ndim))
-        return a, None, None
+        return a
 
     def rec_tok(a, offsets):
         a = np.asarray(a, np.float64)
         calls.append(("tokens", a.shape, tuple(int(o) for o in offsets), a.copy()))
         return a
 
-    monkeypatch.setattr(orc, "mx_quant_dequant", rec)
+    monkeypatch.setattr(orc, "mx_dequant", rec)
     monkeypatch.setattr(orc, "mx_quant_dequant_tokens", rec_tok)
     out = orc.expert_backward_mxfp8(dYp, Xp, g, w13e, w2e, fwd)
     row_calls = sorted((c[1], c[2]) for c in calls if c[0] == "rows")
@@ -163,7 +195,7 @@ def test_mxfp8_forward_with_identity_quantiser_is_exact(monkeypatch):
     inp = mi.make_inputs(d, 8)
     r = orc.route(inp["logits"], d.k)
     Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
-    monkeypatch.setattr(orc, "mx_quant_dequant", lambda a, axis=-1: (np.asarray(a, np.float64), None, None))
+    monkeypatch.setattr(orc, "mx_dequant", lambda a, axis=-1: np.asarray(a, np.float64))
     Yq, stq = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r)
     assert np.max(np.abs(Yq - Y)) <= 1e-12 * np.max(np.abs(Y))
     for key in ("G1", "G3", "A", "O"):
@@ -178,9 +210,9 @@ def test_mxfp8_forward_operands_blocked_along_k(monkeypatch):
     def rec(a, axis=-1):
         a = np.asarray(a, np.float64)
         calls.append((a.shape, axis % a.ndim))
-        return a, None, None
+        return a
 
-    monkeypatch.setattr(orc, "mx_quant_dequant", rec)
+    monkeypatch.setattr(orc, "mx_dequant", rec)
     orc.expert_forward_mxfp8(rng.standard_normal((n, H)), rng.standard_normal((2 * I, H)),
                              rng.standard_normal((H, I)))
     # x [n, H] and W13 [2I, H] along H; A [n, I] and W2 [H, I] along I
