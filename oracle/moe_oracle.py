@@ -162,6 +162,21 @@ def expert_backward(dO: np.ndarray, xrows: np.ndarray, w13e: np.ndarray, w2e: np
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
+def _for_each_expert(r: Routing, body, workers: int = 1):
+    """body(e, a, b) for every non-empty expert segment [a, b).  The bodies
+    write disjoint rows and experts, so running them on `workers` threads
+    (numpy releases the GIL in its kernels) gives the same arrays."""
+    segs = [(e, a, b) for e, a, b in _segments(r) if b > a]
+    if workers <= 1:
+        for seg in segs:
+            body(*seg)
+        return
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(body, *seg) for seg in segs]:
+            f.result()
+
+
 def _segments(r: Routing):
     for e in range(r.E):
         a, b = int(r.offsets[e]), int(r.offsets[e + 1])
@@ -186,15 +201,16 @@ def forward_with_gates(x, w13, w2, idx, gate):
     return forward(x, w13, w2, r)
 
 
-def forward(x, w13, w2, r: Routing):
+def forward(x, w13, w2, r: Routing, *, workers: int = 1):
     """Y[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]) through the permuted layout.
 
     Returns (Y [T,H] float64, state) where state keeps what the backward needs.
+    workers > 1 runs the independent experts on that many threads (same result).
     """
-    return _layer_forward(x, w13, w2, r, expert_forward)
+    return _layer_forward(x, w13, w2, r, expert_forward, workers)
 
 
-def _layer_forward(x, w13, w2, r: Routing, expert_fn):
+def _layer_forward(x, w13, w2, r: Routing, expert_fn, workers: int = 1):
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
     k = r.k
@@ -205,11 +221,11 @@ def _layer_forward(x, w13, w2, r: Routing, expert_fn):
     G1 = np.zeros((M, I))
     G3 = np.zeros((M, I))
     A = np.zeros((M, I))
-    for e, a, b in _segments(r):
-        if b == a:
-            continue
+    def one(e, a, b):
         f = expert_fn(x[tok[a:b]], w13[e], w2[e])
         O[a:b], G1[a:b], G3[a:b], A[a:b] = f["O"], f["G1"], f["G3"], f["A"]
+
+    _for_each_expert(r, one, workers)
     # combine: gather each token's k rows back in slot order, weight by its gates
     Orows = O[r.flat_to_sorted].reshape(T, k, H)
     Y = np.einsum("tk,tkh->th", r.gate, Orows)
@@ -241,8 +257,9 @@ def router_projection_backward(dlogits: np.ndarray, x: np.ndarray, w_router: np.
             "dw_router": dl.T @ np.asarray(x, dtype=np.float64)}
 
 
-def backward(dy, x, w13, w2, r: Routing, state: dict, *, want_dw=True):
-    """Gradients of <dY, Y> with respect to x, W13, W2, the gates and the logits."""
+def backward(dy, x, w13, w2, r: Routing, state: dict, *, want_dw=True, workers: int = 1):
+    """Gradients of <dY, Y> with respect to x, W13, W2, the gates and the logits
+    (workers > 1: the independent experts on that many threads, same result)."""
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -258,14 +275,14 @@ def backward(dy, x, w13, w2, r: Routing, state: dict, *, want_dw=True):
     dXp = np.zeros((M, H))
     dW13 = np.zeros(w13.shape) if want_dw else None
     dW2 = np.zeros(w2.shape) if want_dw else None
-    for e, a, b in _segments(r):
-        if b == a:
-            continue            # an expert with no rows has zero weight gradients
+    def one(e, a, b):           # an expert with no rows keeps zero weight gradients
         fwd = {"G1": state["G1"][a:b], "G3": state["G3"][a:b], "A": state["A"][a:b]}
         g = expert_backward(dO[a:b], x[tok[a:b]], w13[e], w2[e], fwd)
         dXp[a:b] = g["dX"]
         if want_dw:
             dW13[e], dW2[e] = g["dW13"], g["dW2"]
+
+    _for_each_expert(r, one, workers)
     # unpermute + sum over the k slots
     dX = dXp[r.flat_to_sorted].reshape(T, k, H).sum(axis=1)
     dlogits = router_backward(r.gate, dgate, r.idx, E)
@@ -330,8 +347,8 @@ def e4m3fn_round(v: np.ndarray) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     a = np.minimum(np.abs(v), 448.0)
     _, ex = np.frexp(a)                         # a = m * 2**ex, m in [0.5, 1): binade e = ex - 1
-    step_exp = np.maximum(ex - 1, -6) - 3
-    r = np.ldexp(np.round(np.ldexp(a, -step_exp)), step_exp)
+    step = np.exp2((np.maximum(ex, -5) - 4).astype(np.float64))   # 2**(max(e, -6) - 3)
+    r = np.round(a / step) * step
     return np.copysign(r, v)
 
 
@@ -378,8 +395,8 @@ def mx_dequant(a: np.ndarray, axis: int = -1) -> np.ndarray:
     n = a_m.shape[-1]
     assert n % 32 == 0
     blk = a_m.reshape(a_m.shape[:-1] + (n // 32, 32))
-    X = mx_scale_exponent(np.max(np.abs(blk), axis=-1))[..., None]
-    deq = np.ldexp(e4m3fn_round(np.ldexp(blk, -X)), X)
+    scale = np.exp2(mx_scale_exponent(np.max(np.abs(blk), axis=-1)).astype(np.float64))[..., None]
+    deq = e4m3fn_round(blk / scale) * scale
     return np.moveaxis(deq.reshape(a_m.shape), -1, axis)
 
 
@@ -434,10 +451,10 @@ def expert_backward_mxfp8(dYp, Xp, g, w13e, w2e, fwd: dict) -> dict:
     return {"dXp": dXp, "dgate": dgate, "dG": dG, "dW2": dW2, "dW13": dW13}
 
 
-def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
+def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict, *, workers: int = 1):
     """fp8_bwd backward of the whole layer: expert_backward_mxfp8 on every
     expert segment, then the unpermute-reduce of dX and the router backward
-    exactly as in backward()."""
+    exactly as in backward() (workers > 1: experts on that many threads)."""
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -449,15 +466,15 @@ def backward_mxfp8(dy, x, w13, w2, r: Routing, state: dict):
     dW13 = np.zeros(w13.shape)
     dW2 = np.zeros(w2.shape)
     dgate_sorted = np.zeros(M)
-    for e, a, b in _segments(r):
-        if b == a:
-            continue
+    def one(e, a, b):
         fwd = {key: state[key][a:b] for key in ("A", "G1", "G3")}
         out = expert_backward_mxfp8(dy[tok[a:b]], x[tok[a:b]], g_sorted[a:b], w13[e], w2[e], fwd)
         dXp[a:b] = out["dXp"]
         dgate_sorted[a:b] = out["dgate"]
         dW2[e] = out["dW2"]
         dW13[e] = out["dW13"]
+
+    _for_each_expert(r, one, workers)
     dX = dXp[r.flat_to_sorted].reshape(T, k, H).sum(axis=1)
     dgate = dgate_sorted[r.flat_to_sorted].reshape(T, k)
     dlogits = router_backward(r.gate, dgate, r.idx, E)
@@ -480,7 +497,7 @@ def expert_forward_mxfp8(xrows, w13e, w2e) -> dict:
     return {"G1": G1, "G3": G3, "A": A, "O": O}
 
 
-def forward_mxfp8(x, w13, w2, r: Routing):
+def forward_mxfp8(x, w13, w2, r: Routing, *, workers: int = 1):
     """Layer forward of the mxfp8 mode: forward() with expert_forward_mxfp8.
     Its backward is backward_mxfp8 applied to the state returned here."""
-    return _layer_forward(x, w13, w2, r, expert_forward_mxfp8)
+    return _layer_forward(x, w13, w2, r, expert_forward_mxfp8, workers)

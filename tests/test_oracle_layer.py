@@ -242,3 +242,24 @@ def test_router_projection_finite_differences():
     assert checks >= 10
     # the router's share of dx is not negligible here (the pin would miss a dropped term)
     assert np.abs(pr["dx"]).max() > 1e-3 * np.abs(g["dx"]).max()
+
+
+def test_threaded_experts_give_the_same_arrays():
+    """workers > 1 only schedules the independent experts on threads: every
+    output of forward, backward and the quantised backward is bitwise the
+    single-threaded one."""
+    d = mi.LayerDims(T=300, H=128, I=64, E=8, k=2, dtype="bf16", skew=True)
+    inp = mi.make_inputs(d, 21)
+    r = orc.route(inp["logits"], d.k)
+    Y1, s1 = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    Y4, s4 = orc.forward(inp["x"], inp["w13"], inp["w2"], r, workers=4)
+    assert np.array_equal(Y1, Y4) and all(np.array_equal(s1[k], s4[k]) for k in s1)
+    b1 = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, s1)
+    b4 = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, s1, workers=4)
+    q1 = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, s1)
+    q4 = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, s1, workers=4)
+    for a, b in ((b1, b4), (q1, q4)):
+        assert all(np.array_equal(a[k], b[k]) for k in a)
+    m1, _ = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r)
+    m4, _ = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r, workers=4)
+    assert np.array_equal(m1, m4)
