@@ -233,87 +233,73 @@ def copy_calibration(mib: int):
     del src, dst
 
 
-def cpu_baseline(d, inp, n_tokens):
-    """The fp64 oracle on the first n_tokens tokens of the same batch (all experts)."""
-    import numpy as np
-    from oracle import moe_oracle as orc
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS library numpy calls, with
+    the threads it uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 0) for i in threadpool_info()] or [os.cpu_count()])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+            threads = max(int(i.get("num_threads", 0)) for i in libs)
     except Exception:
-        cores = os.cpu_count()
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(d, inp, n_tokens):
+    """The fp64 oracle on the first n_tokens tokens of the same batch (all
+    experts, same weights): route, forward and backward timed separately."""
+    from oracle import moe_oracle as orc
+    model, blas, cores = cpu_info()
     n = min(n_tokens, d.T)
     x, L, dy = inp["x"][:n], inp["logits"][:n], inp["dy"][:n]
     t0 = time.perf_counter()
     r = orc.route(L, d.k)
+    t1 = time.perf_counter()
     Y, st = orc.forward(x, inp["w13"], inp["w2"], r)
+    t2 = time.perf_counter()
     orc.backward(dy, x, inp["w13"], inp["w2"], r, st)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     flops = 18.0 * n * d.k * d.H * d.I
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "route_s": round(t1 - t0, 3), "forward_s": round(t2 - t1, 3), "backward_s": round(t3 - t2, 3),
+            "cpu_model": model, "blas": blas,
             "sample": f"fp64 NumPy oracle, route+forward+backward of the first {n} of {d.T} tokens "
                       f"(all {d.E} experts, same weights), {dt:.2f} s wall"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--mode", choices=["bf16", "mxfp8", "fp8_bwd"], default=None,
-                    help="run the configuration's shape in another precision mode")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the router projection and accumulate-into timings that follow the steps "
-                         "(profiled runs: every GEMM launch is then a plain step's)")
-    ap.add_argument("--vendor-ceiling", action="store_true",
-                    help="also time hipBLASLt on the per-expert GEMM shapes (roofline context)")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="run one plain copy of this many MiB before the timed region (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
-              f"(this build runs on a single MI355X and has no multi-GPU path).", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-    import moe_inputs as mi
-    import grouped_gemm_layer_amd as g
-
-    d = mi.CONFIGS[args.config]
-    workload = mi.CONFIG_NAMES[args.config]
-    if args.mode is not None and args.mode != d.run_mode:
-        import dataclasses
-        d = dataclasses.replace(d, mode=args.mode)
-        workload += f", {args.mode} mode"
-    seed = args.config if args.seed is None else args.seed
-    print(f"[bench] config {args.config}: {workload}", file=sys.stderr, flush=True)
-    inp = mi.make_inputs(d, seed)
-    torch.cuda.set_device(0)
-    layer = g.MoeLayer(d.T, d.H, d.I, d.E, d.k, mode=d.run_mode)
-    adt = layer.act_dtype
-    dev = lambda a, dt: torch.from_numpy(a).to(device="cuda", dtype=dt)
-    x, w13, w2, dy = dev(inp["x"], adt), dev(inp["w13"], adt), dev(inp["w2"], adt), dev(inp["dy"], adt)
-    logits = dev(inp["logits"], torch.float32)
-    torch.cuda.synchronize()
-    if args.copy_calibration_mib > 0:
-        copy_calibration(args.copy_calibration_mib)
-
-    ev = HipEvents()
-    nf, nb = g.num_kernels(layer.dims, "forward"), g.num_kernels(layer.dims, "backward")
-    fp8_bwd = d.run_mode in ("fp8_bwd", "mxfp8")
-    fp8_fwd = d.run_mode == "mxfp8"
+def kernel_names(mode):
+    fp8_bwd = mode in ("fp8_bwd", "mxfp8")
+    fp8_fwd = mode == "mxfp8"
     fwd_names = FWD_KERNELS_MX8 if fp8_fwd else FWD_KERNELS
     bwd_names = BWD_KERNELS_MXFP8 if fp8_fwd else BWD_KERNELS_FP8 if fp8_bwd else BWD_KERNELS
-    assert nf == len(fwd_names) and nb == len(bwd_names)
     fp8_gemms = (("gemm1_swiglu", "gemm2") if fp8_fwd else ()) + \
         (("dgrad2_dswiglu", "dgrad1", "wgrad2", "wgrad1") if fp8_bwd else ())
     peak = {n: (PEAK_FP8_TFLOPS if n in fp8_gemms else PEAK_BF16_TFLOPS) for n in fwd_names + bwd_names}
-    K, W = args.steps, args.warmup
+    return fwd_names, bwd_names, peak
+
+
+def time_steps(g, layer, d, x, w13, w2, dy, logits, K, W, ev):
+    """W untimed steps, then K timed ones (route + forward + backward), the
+    whole region bracketed by device synchronisations; per-kernel durations
+    from the events the library records between its kernels."""
+    import numpy as np
+    import torch
+    fwd_names, bwd_names, peak = kernel_names(d.run_mode)
+    nf, nb = g.num_kernels(layer.dims, "forward"), g.num_kernels(layer.dims, "backward")
+    assert nf == len(fwd_names) and nb == len(bwd_names)
     fev = [ev.create(nf + 1) for _ in range(K)]
     bev = [ev.create(nb + 1) for _ in range(K)]
     rstart = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -366,31 +352,144 @@ def main():
             ent.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
         kernels[n] = ent
     total_flops = 18.0 * d.M * d.H * d.I
-    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = sum(avg[n] for n in flops)
+    fwd, bwd, rte = float(np.mean(fwd_ms)), float(np.mean(bwd_ms)), float(np.mean(route_ms))
+    return {
+        "ms_per_step": ms_per_step, "value": total_flops / (ms_per_step * 1e-3) / 1e12,
+        "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "route_ms": round(rte, 4),
+        # the pages' "full layer" timing recomputes the forward (activation checkpointing)
+        "ms_2f_plus_b": round(2.0 * fwd + bwd + rte, 4),
+        "fwd_tflops": round(6.0 * d.M * d.H * d.I / (fwd * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(12.0 * d.M * d.H * d.I / (bwd * 1e-3) / 1e12, 1),
+        "gemm_tflops": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_mfma_frac": round(sum(flops[n] / (peak[n] * 1e12) for n in flops) / (gemm_ms * 1e-3), 4),
+        "kernels": kernels, "_avg": avg, "_peak": peak, "_flops": flops,
+    }
+
+
+# Extra workloads timed after the headline (compact figures): the skewed
+# routing, the Qwen3-235B-A22B shape, the fp8_bwd mode and the mxfp8 mode.
+EXTRA_WORKLOADS = [(3, None), (4, None), (5, None), (2, "mxfp8")]
+
+
+def time_extra(g, mi, cfg, mode, base, K, W, ev):
+    """Steps of one extra workload, with its own seeded inputs (seed = the
+    configuration number); the 30B-shape workloads reuse the headline's
+    device tensors of the same recipe where only the seed would differ, except
+    the logits, which carry the routing."""
+    import dataclasses
+    import torch
+    d = mi.CONFIGS[cfg]
+    name = mi.CONFIG_NAMES[cfg]
+    if mode is not None:
+        d = dataclasses.replace(d, mode=mode)
+        name += f", {mode} mode"
+    print(f"[bench] extra: config {cfg}{'' if mode is None else ' ' + mode}: {name}", file=sys.stderr, flush=True)
+    same_shape = (d.T, d.H, d.I, d.E, d.k) == tuple(base["dims"])
+    inp = mi.make_inputs(d, cfg, want=("logits",) if same_shape else ("x", "w13", "w2", "logits", "dy"))
+    dev = lambda a, dt: torch.from_numpy(a).to(device="cuda", dtype=dt)
+    if same_shape:
+        x, w13, w2, dy = base["x"], base["w13"], base["w2"], base["dy"]
+        note = "x, W13, W2, dY: the headline's tensors (same recipe, seed 2); logits of this configuration"
+    else:
+        x, w13, w2, dy = (dev(inp[k], torch.bfloat16) for k in ("x", "w13", "w2", "dy"))
+        note = f"inputs of this configuration (seed {cfg})"
+    logits = dev(inp["logits"], torch.float32)
+    del inp
+    layer = g.MoeLayer(d.T, d.H, d.I, d.E, d.k, mode=d.run_mode)
+    res = time_steps(g, layer, d, x, w13, w2, dy, logits, K, W, ev)
+    counts = layer.routing.counts.cpu()
+    out = {"workload": name, "mode": d.run_mode, "T": d.T, "H": d.H, "I": d.I, "E": d.E, "k": d.k,
+           "ms_per_step": round(res["ms_per_step"], 4), "tflops": round(res["value"], 1),
+           "fwd_ms": res["fwd_ms"], "bwd_ms": res["bwd_ms"], "route_ms": res["route_ms"],
+           "ms_2f_plus_b": res["ms_2f_plus_b"], "gemm_tflops": res["gemm_tflops"],
+           "gemm_mfma_frac": res["gemm_mfma_frac"],
+           "gemm_ms": {n: v["ms"] for n, v in res["kernels"].items() if n in res["_flops"]},
+           "gemm_frac": {n: v["mfma_frac"] for n, v in res["kernels"].items() if n in res["_flops"]},
+           "routing": {"max_over_mean": round(float(counts.max()) * d.E / d.M, 2),
+                       "empty_experts": int((counts == 0).sum())},
+           "inputs": note}
+    other = {n: v["ms"] for n, v in res["kernels"].items() if n not in res["_flops"] and v["ms"] >= 0.02}
+    if other:
+        out["other_kernels_ms"] = other
+    del layer, x, w13, w2, dy, logits
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--mode", choices=["bf16", "mxfp8", "fp8_bwd"], default=None,
+                    help="run the configuration's shape in another precision mode")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip everything after the headline steps: the router projection, accumulate-into "
+                         "and checkpointing timings and the other workloads (profiled runs: every GEMM launch "
+                         "is then a plain step's)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads (skewed routing, 235B shape, fp8_bwd, mxfp8)")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed steps per extra workload")
+    ap.add_argument("--vendor-ceiling", action="store_true",
+                    help="also time hipBLASLt on the per-expert GEMM shapes (roofline context)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB before the timed region (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X and has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    import grouped_gemm_layer_amd as g
+
+    d = mi.CONFIGS[args.config]
+    workload = mi.CONFIG_NAMES[args.config]
+    if args.mode is not None and args.mode != d.run_mode:
+        import dataclasses
+        d = dataclasses.replace(d, mode=args.mode)
+        workload += f", {args.mode} mode"
+    seed = args.config if args.seed is None else args.seed
+    print(f"[bench] config {args.config}: {workload}", file=sys.stderr, flush=True)
+    inp = mi.make_inputs(d, seed)
+    torch.cuda.set_device(0)
+    layer = g.MoeLayer(d.T, d.H, d.I, d.E, d.k, mode=d.run_mode)
+    adt = layer.act_dtype
+    dev = lambda a, dt: torch.from_numpy(a).to(device="cuda", dtype=dt)
+    x, w13, w2, dy = dev(inp["x"], adt), dev(inp["w13"], adt), dev(inp["w2"], adt), dev(inp["dy"], adt)
+    logits = dev(inp["logits"], torch.float32)
+    torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    res = time_steps(g, layer, d, x, w13, w2, dy, logits, K, W, ev)
+    avg, peak, flops = res["_avg"], res["_peak"], res["_flops"]
     dom = max(flops, key=lambda n: avg[n])
     dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2), "peak": peak[dom],
                 "unit": "TFLOP/s", "frac": round(dom_tf / peak[dom], 4),
                 "traffic": recorded_traffic(args.config, dom),
                 "flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
-    gemm_ms = sum(avg[n] for n in flops)
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "metric": METRIC, "value": round(res["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
         "dtype": {"fp32": "f32", "bf16": "bf16", "fp8_bwd": "bf16 fwd + mxfp8 bwd", "mxfp8": "mxfp8"}[d.run_mode],
         "data": "synthetic",
         "config": {"workload": workload, "T": d.T, "H": d.H, "I": d.I, "E": d.E,
                    "k": d.k, "mode": d.run_mode, "seed": seed},
-        "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4),
-        "route_ms": round(float(np.mean(route_ms)), 4),
-        # the pages' "full layer" timing recomputes the forward (activation checkpointing)
-        "ms_2f_plus_b": round(2.0 * float(np.mean(fwd_ms)) + float(np.mean(bwd_ms)) + float(np.mean(route_ms)), 4),
-        "fwd_tflops": round(6.0 * d.M * d.H * d.I / (np.mean(fwd_ms) * 1e-3) / 1e12, 1),
-        "bwd_tflops": round(12.0 * d.M * d.H * d.I / (np.mean(bwd_ms) * 1e-3) / 1e12, 1),
-        "gemm_tflops": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
-        "gemm_mfma_frac": round(sum(flops[n] / (peak[n] * 1e12) for n in flops) / (gemm_ms * 1e-3), 4),
-        "kernels": kernels, "roofline": roofline, "cpu_baseline": None,
     }
+    out.update({k: v for k, v in res.items() if not k.startswith("_") and k not in ("ms_per_step", "value")})
+    out.update({"roofline": roofline, "cpu_baseline": None})
     if not args.no_extras:
         if d.run_mode != "fp32":   # the router projection (x W_r^T -> route; its backward), timed on its own
             out["router_projection"] = time_router_projection(g, layer, d, x, seed, K, W)
@@ -405,6 +504,12 @@ def main():
         out["ms_checkpointed_step"] = round(out["route_ms"] + nosave + rec + out["bwd_ms"], 4)
     if args.vendor_ceiling:
         out["vendor_ceiling"] = vendor_ceiling(d)
+    if not args.no_extras and not args.no_workloads and args.config == 2 and args.mode is None:
+        del layer
+        torch.cuda.empty_cache()
+        base = {"dims": (d.T, d.H, d.I, d.E, d.k), "x": x, "w13": w13, "w2": w2, "dy": dy}
+        out["workloads"] = [time_extra(g, mi, cfg, mode, base, args.extra_steps, min(W, 3), ev)
+                            for cfg, mode in EXTRA_WORKLOADS]
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_tokens)

@@ -1,29 +1,27 @@
 """GPU parity at the full layer shapes (Qwen3-30B-A3B and Qwen3-235B-A22B
 expert shapes, T=16384, E=128, top-8), in the launch configuration the
-benchmark times.
+benchmark times, compared with the fp64 oracle over every element.
 
-Routing is compared bit-exactly in full.  The fp64 oracle cannot run the
-whole layer here in seconds, so it evaluates sampled outputs one by one:
-Y, dX, dgate and dlogits of sampled tokens (rows are independent), and the
-weight gradients of sampled experts (the most loaded one, a median one and,
-with skewed routing, an empty one).  Properties that hold at any size are
-checked over every output: the Euler identities <dW2,W2> = <dW3,W3> =
-<dgate,gate> = <dY,Y> and the zero row-sum of dlogits.
+Routing is compared bit-exactly.  y, dX, dW13, dW2, dgate and dlogits are
+compared whole: max|gpu - ref| / max|ref| per tensor against the bf16 bar
+2e-2, and the weight gradients of every empty expert must be exactly zero.
+The Euler identities <dW2,W2> = <dW3,W3> = <dgate,gate> = <dY,Y> and the
+zero row-sum of dlogits are checked as properties that hold at any size.
 """
 import numpy as np
 import pytest
 
 import moe_inputs as mi
 from oracle import moe_oracle as orc
-from _layer_harness import (GpuRun, relerr, to_np, check_routing_exact, oracle_token_rows,
-                            oracle_expert_wgrad)
+from _layer_harness import GpuRun, relerr, to_np, check_routing_exact, record_errors
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_fullsize_sampled(cfg):
+def test_fullsize_whole(cfg):
     import torch
     d = mi.CONFIGS[cfg]
     print(f"[fullsize] config {cfg}: {mi.CONFIG_NAMES[cfg]}", flush=True)
@@ -39,32 +37,7 @@ def test_fullsize_sampled(cfg):
         print(f"[fullsize] skew: max/mean {r.counts.max() / mean:.1f}, empty experts "
               f"{int((r.counts == 0).sum())}", flush=True)
 
-    rng = np.random.default_rng(1000 + cfg)
-    tokens = np.unique(np.concatenate([rng.choice(d.T, 30, replace=False), [0, d.T - 1]]))
-    ref = oracle_token_rows(orc, inp, r, tokens)
-    tt = torch.as_tensor(tokens, device="cuda")
-    errs = {
-        "y": relerr(to_np(L.y[tt]), ref["y"]),
-        "dx": relerr(to_np(L.dx[tt]), ref["dx"]),
-        "dgate": relerr(to_np(L.dgate[tt]), ref["dgate"]),
-        "dlogits": relerr(to_np(L.dlogits[tt]), ref["dlogits"]),
-    }
-    order = np.argsort(r.counts, kind="stable")
-    experts = [int(order[-1]), int(order[d.E // 2])]
-    if (r.counts == 0).any():
-        experts.append(int(np.nonzero(r.counts == 0)[0][0]))
-    for e in experts:
-        w = oracle_expert_wgrad(orc, inp, r, e)
-        if r.counts[e] == 0:
-            assert torch.count_nonzero(L.dw13[e]).item() == 0 and torch.count_nonzero(L.dw2[e]).item() == 0
-            continue
-        errs[f"dw13[{e}]"] = relerr(to_np(L.dw13[e]), w["dw13"])
-        errs[f"dw2[{e}]"] = relerr(to_np(L.dw2[e]), w["dw2"])
-    print("[fullsize] sampled errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    for k, v in errs.items():
-        assert v <= TOL, (k, v)
-
-    # Euler identities over all outputs, in float64 on the device
+    # properties over every output, in float64 on the device
     f64 = torch.float64
     I = d.I
     dyY = torch.sum(run.dy.to(f64) * L.y.to(f64)).item()
@@ -76,3 +49,18 @@ def test_fullsize_sampled(cfg):
         assert abs(v - dyY) <= 2e-2 * abs(dyY)
     rowsum = L.dlogits.to(f64).sum(dim=1).abs().max().item()
     assert rowsum <= 1e-5 * L.dlogits.abs().max().item() * d.k
+    empty = np.nonzero(r.counts == 0)[0]
+    for e in empty:
+        assert torch.count_nonzero(L.dw13[int(e)]).item() == 0 and torch.count_nonzero(L.dw2[int(e)]).item() == 0
+
+    # the whole layer through the oracle
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    errs = {"y": relerr(to_np(L.y), Y)}
+    del Y
+    ref = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    del st
+    for key, t in (("dx", L.dx), ("dgate", L.dgate), ("dlogits", L.dlogits), ("dw2", L.dw2), ("dw13", L.dw13)):
+        errs[key] = relerr(to_np(t), ref.pop(key))
+    record_errors(f"fullsize/config{cfg}", errs, {k: TOL for k in errs})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)

@@ -10,7 +10,7 @@ import pytest
 
 import moe_inputs as mi
 from oracle import moe_oracle as orc
-from _layer_harness import GpuRun, relerr, to_np, check_routing_exact
+from _layer_harness import GpuRun, relerr, to_np, check_routing_exact, record_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,8 @@ def _full_compare(dims, inp, tol):
         "dgate": relerr(to_np(L.dgate), g["dgate"]),
         "dlogits": relerr(to_np(L.dlogits), g["dlogits"]),
     }
-    print("[parity] errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    record_errors(f"parity/{dims.run_mode}/T{dims.T}_H{dims.H}_I{dims.I}_E{dims.E}_k{dims.k}"
+                  + ("_skew" if dims.skew else ""), errs, {k: tol for k in errs})
     for key, v in errs.items():
         assert v <= tol, (key, v)
     # empty experts have exactly zero weight gradients
@@ -103,7 +104,11 @@ def test_backward_accumulate_into(dims, seed):
     hold: against the plain backward's result G and a random start R, an
     expert in one chunk gives R + G exactly (one fp32 add per element; empty
     experts keep R), a split expert (R + chunk 0) + chunk 1 ... within fp32
-    rounding; every other output is bitwise that of the plain backward."""
+    rounding; every other output is bitwise that of the plain backward.  And
+    against the oracle: (result - R) matches the oracle's dW13 and dW2 within
+    the mode's bar (bf16 2e-2; fp8_bwd: the quantised oracle's bar, and
+    against the exact backward 6e-2 or the definition's own error plus that
+    bar, whichever is larger)."""
     import torch
     inp = mi.make_inputs(dims, seed)
     if dims.T == 9000:
@@ -116,8 +121,8 @@ def test_backward_accumulate_into(dims, seed):
     G13, G2 = L.dw13.clone(), L.dw2.clone()
     others = [t.clone() for t in (L.dx, L.dgate, L.dlogits)]
     gen = torch.Generator(device="cuda").manual_seed(seed)
-    R13 = torch.randn(G13.shape, device="cuda", generator=gen)
-    R2 = torch.randn(G2.shape, device="cuda", generator=gen)
+    R13 = torch.randn(G13.shape, device="cuda", generator=gen) * G13.abs().max()
+    R2 = torch.randn(G2.shape, device="cuda", generator=gen) * G2.abs().max()
     L.dw13.copy_(R13)
     L.dw2.copy_(R2)
     run.layer.backward(run.dy, run.x, run.w13, run.w2, accumulate=True)
@@ -132,6 +137,28 @@ def test_backward_accumulate_into(dims, seed):
             else:
                 err = (got[e] - (R[e] + G[e])).abs().max().item()
                 assert err <= 1e-5 * (R[e].abs().max().item() + G[e].abs().max().item()), (e, err)
+    # the accumulated gradients against the oracle
+    r = orc.route(inp["logits"], dims.k)
+    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+    exact = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+    added = {"dw13": to_np(L.dw13) - to_np(R13), "dw2": to_np(L.dw2) - to_np(R2)}
+    tag = f"accumulate/{dims.run_mode}/T{dims.T}_E{dims.E}_k{dims.k}"
+    if dims.run_mode == "fp8_bwd":
+        from test_gpu_mxfp8 import TOL_EXACT, TOL_QORACLE
+        quant = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+        e_q = {k: relerr(v, quant[k]) for k, v in added.items()}
+        e_x = {k: relerr(v, exact[k]) for k, v in added.items()}
+        bars_x = {k: max(TOL_EXACT, relerr(quant[k], exact[k]) + TOL_QORACLE[k]) for k in added}
+        record_errors(tag + "/vs_quantised", e_q, TOL_QORACLE)
+        record_errors(tag + "/vs_exact", e_x, bars_x)
+        for k in added:
+            assert e_q[k] <= TOL_QORACLE[k] and e_x[k] <= bars_x[k], (k, e_q[k], e_x[k])
+    else:
+        tol = TOL["fp32"] if dims.run_mode == "fp32" else TOL["bf16"]
+        errs = {k: relerr(v, exact[k]) for k, v in added.items()}
+        record_errors(tag, errs, {k: tol for k in errs})
+        for k, v in errs.items():
+            assert v <= tol, (k, v)
 
 
 def test_edge_single_token():
