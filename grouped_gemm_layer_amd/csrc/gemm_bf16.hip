@@ -379,7 +379,118 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
   if constexpr (gathered_k) {
     if (nk > 0) { fill_tok(0); __syncthreads(); }
   }
-  {
+  // A wave whose rows all lie past the expert's end (the ragged last tile)
+  // computes nothing it would store: it keeps its share of the DMA and the
+  // barriers and skips its fragment reads and MFMAs.
+  const bool idle = K_::ragged_rows && __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
+  if constexpr (C::PIPE) {
+    // Software pipeline over 32-wide K steps: the fragments of the next step
+    // are read from LDS while the MFMAs of the current one run.  One barrier
+    // per K tile, before its last step: it publishes tile kt + 1 (every
+    // wave's DMA of it has landed) and frees the stage of tile kt (every
+    // wave has read its fragments), which then receives tile kt + S while the
+    // last step's MFMAs run; the first step of tile kt + 1 is read meanwhile.
+    constexpr int KS = BK / 32, ND = DA + DB;
+    typedef bf16x8_t AStep[FM];
+    typedef bf16x8_t BStep[FN];
+    auto read_step = [&](int st, int ks, AStep& a_, BStep& b_) __attribute__((always_inline)) {
+      const bf16_t* As = smem + st * STAGE;
+      const bf16_t* Bs = As + BM * BK;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (K_::a_ko) a_[i] = frag_ko<BM>(As, wm * WM + 16 * i, ks, lane);
+        else a_[i] = frag_kc<BK>(As, wm * WM + 16 * i, ks, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (K_::b_ko) b_[j] = frag_ko<BN>(Bs, brow(j), ks, lane);
+        else b_[j] = frag_kc<BK>(Bs, brow(j), ks, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs they overlap
+    };
+    auto mfma_step = [&](const AStep& a_, const BStep& b_) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_[j], a_[i], acc[i][j], 0, 0, 0);
+    };
+    // the last step's MFMAs with the DMA of tile kt into stage st spread between them
+    auto mfma_step_dma = [&](const AStep& a_, const BStep& b_, int kt, int st) __attribute__((always_inline)) {
+      constexpr int NM = FM * FN;
+      constexpr int SP = NM / ND > 0 ? NM / ND : 1;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int idx = i * FN + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_[j], a_[i], acc[i][j], 0, 0, 0);
+          if (idx % SP == SP - 1 && idx / SP < ND) {
+            issue_one(kt, st, idx / SP);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+      for (int q = NM / SP; q < ND; ++q) issue_one(kt, st, q);
+    };
+    // lgkmcnt(0) as a builtin (vmcnt and expcnt fields at their maxima), so
+    // that the compiler knows every LDS read has completed
+    auto lds_wait_all = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xC07F); };
+
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue_tile(st, st);
+    vm_wait<(S - 1) * ND>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int st_c = 0;
+    // the barrier of tile kt: this wave's reads of the tile are complete and
+    // its DMA of tile kt + 1 has landed, then the block synchronises
+    auto publish = [&](int kt) __attribute__((always_inline)) {
+      lds_wait_all();
+      vm_wait<(S - 2) * ND>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      refill_tok(kt + S);
+    };
+    if (idle) {   // the same barriers and DMA, no reads or MFMAs
+      for (int kt = 0; kt < nk; ++kt) {
+        publish(kt);
+        issue_tile(kt + S, st_c);
+        st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+      }
+    } else if constexpr (KS == 2) {
+      AStep a0, a1;
+      BStep b0, b1;
+      read_step(0, 0, a0, b0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int st_n = (st_c + 1 == S) ? 0 : st_c + 1;
+        read_step(st_c, 1, a1, b1);         // step 1 of this tile
+        mfma_step(a0, b0);                  // step 0
+        publish(kt);
+        read_step(st_n, 0, a0, b0);         // step 0 of the next tile
+        mfma_step_dma(a1, b1, kt + S, st_c);   // step 1, refilling this tile's stage
+        st_c = st_n;
+      }
+    } else {
+      AStep a0, a1;
+      BStep b0, b1;
+      read_step(0, 0, a0, b0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        const int s1 = (st_c + 1 == S) ? 0 : st_c + 1;
+        publish(kt);
+        read_step(s1, 0, a1, b1);
+        mfma_step_dma(a0, b0, kt + S, st_c);
+        st_c = s1;
+        if (kt + 1 < nk) {
+          const int s2 = (st_c + 1 == S) ? 0 : st_c + 1;
+          publish(kt + 1);
+          read_step(s2, 0, a0, b0);
+          mfma_step_dma(a1, b1, kt + 1 + S, st_c);
+          st_c = s2;
+        }
+      }
+    }
+  } else {
 #pragma unroll
     for (int st = 0; st < S; ++st) issue_tile(st, st);
     // S tiles in flight.  Iteration kt: wait for this wave's DMA of tile kt; a
@@ -388,10 +499,6 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total) {
     // MFMAs run from registers.
     AFrag af;
     BFrag bfr;
-    // A wave whose rows all lie past the expert's end (the ragged last tile)
-    // computes nothing it would store: it keeps its share of the DMA and the
-    // barriers and skips its fragment reads and MFMAs.
-    const bool idle = K_::ragged_rows && __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
     int st_c = 0;
     if (idle) {
       for (int kt = 0; kt < nk; ++kt) {

@@ -60,9 +60,14 @@ __device__ __forceinline__ bool decode_row_tile(const LayerArgs& a, int L, int n
   return true;
 }
 
-template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64, int GD_ = 1>
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64, int GD_ = 1, int PIPE_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
+  // main loop: 0 = every wave reads a whole K tile's fragments between two
+  // barriers, then runs its MFMAs; 1 = software pipeline, the fragments of the
+  // next 32-wide K step are read while the MFMAs of the current one run (one
+  // barrier per K tile)
+  static constexpr int PIPE = PIPE_;
   static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
   static constexpr int STAGES = ST_;    // LDS stages in flight (>= 2)
   static constexpr int NW = WGM * WGN, NTHR = 64 * NW;
@@ -494,7 +499,18 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
 //     codes are staged transposed in LDS and stored as whole 128-byte rows.
 // The values reaching the encoder are those the separate quantisers would
 // read, so the codes are the same.
+// LDS bytes of the dgrad-of-W2 MXFP8 epilogue's staging (gate-gradient
+// partials, transposed code rows and scale bytes of dG13 and g*A)
 template <class C>
+constexpr int dgrad2_mx8_part_bytes() {   // gate-gradient partials of the WGN column waves
+  return C::WGN * C::BM * 4 > 1024 ? C::WGN * C::BM * 4 : 1024;
+}
+template <class C>
+constexpr int dgrad2_mx8_lds_bytes() {
+  return dgrad2_mx8_part_bytes<C>() + 3 * C::BN * (C::BM + 16) + 3 * C::BN * (C::BM / 32);
+}
+
+template <class C, int LDS>
 __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx8Args& q,
                                                     f32x4_t (&acc)[C::FM][C::FN], void* smem, int tid, int lane,
                                                     int wm, int wn, int e, int m0, int mlim, int n0) {
@@ -504,8 +520,10 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
   // staged code rows [column][BM tokens] padded to TS bytes: the 4 column
   // groups of a fragment then fall on different LDS banks
   constexpr int TS = BM + 16;
-  constexpr int T_DG = 1024, T_AG = T_DG + 2 * BN * TS, S_DG = T_AG + BN * TS, S_AG = S_DG + 2 * BN * NB;
-  static_assert(C::WGN * BM * 4 <= T_DG && S_AG + BN * NB <= C::SMEM_BYTES, "staging fits in the operand LDS");
+  constexpr int T_DG = dgrad2_mx8_part_bytes<C>(), T_AG = T_DG + 2 * BN * TS, S_DG = T_AG + BN * TS,
+                S_AG = S_DG + 2 * BN * NB;
+  static_assert(S_AG + BN * NB == dgrad2_mx8_lds_bytes<C>(), "staging layout");
+  static_assert(C::WGN * BM * 4 <= T_DG && S_AG + BN * NB <= LDS, "staging fits in the kernel's LDS");
   uint8_t* lds = static_cast<uint8_t*>(smem);
   const int I = a.I;
   const int mrow = lane & 15, ncol = 4 * (lane >> 4);

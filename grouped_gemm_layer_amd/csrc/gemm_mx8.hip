@@ -34,9 +34,11 @@
 // LDS stage: A codes [BM][128], B codes [BN][128] (16-byte chunks XOR-swizzled
 // by row & 7, conflict-free two-chunk reads), then A scales [BM][4] and B
 // scales [BN][4].  Codes arrive by 16-byte and scales by 4-byte buffer-to-LDS
-// DMA; offsets past a buffer's end read zeros.  Pipeline as in the bf16
-// kernels: STAGES tiles in flight, fragments read into registers between two
-// barriers, then the freed stage is refilled while the MFMAs run.
+// DMA; offsets past a buffer's end read zeros.  Two main loops: as in the
+// bf16 kernels (STAGES tiles in flight, fragments read into registers between
+// two barriers, then the freed stage is refilled while the MFMAs run), or a
+// software pipeline over the wave's 16-row blocks of A with one barrier per K
+// tile (see the PIPE branch).
 #include "gemm_common.h"
 
 namespace moe {
@@ -84,13 +86,20 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   constexpr int NW = C::NW, S = C::STAGES;
   constexpr int DA = BM * ROWB / 1024 / NW, DB = BN * ROWB / 1024 / NW;   // 1 KiB code DMAs per wave
   constexpr int SA = BM * 4 / 256, SB = BN * 4 / 256;                     // 256-byte scale DMAs per tile
-  constexpr int DS = (SA + SB) / NW;                                      // scale DMAs per wave
+  // scale DMAs per wave; when they do not split evenly over the waves, the
+  // spare ones read zeros (an offset past the buffer) into a pad block, so
+  // that every wave issues the same number of DMA instructions per tile
+  constexpr int DS = (SA + SB + NW - 1) / NW;
   static_assert(DA * NW * 1024 == BM * ROWB && DB * NW * 1024 == BN * ROWB, "code tiles split into 1 KiB DMAs");
-  static_assert(SA * 256 == BM * 4 && SB * 256 == BN * 4 && DS * NW == SA + SB, "scale DMAs spread evenly");
+  static_assert(SA * 256 == BM * 4 && SB * 256 == BN * 4, "scale rows split into 256-byte DMAs");
   constexpr int A_CODES = 0, B_CODES = BM * ROWB, A_SC = (BM + BN) * ROWB, B_SC = A_SC + BM * 4;
-  constexpr int STAGE = (BM + BN) * (ROWB + 4);
+  constexpr int PAD = B_SC + BN * 4;                                      // pad block of the spare scale DMAs
+  constexpr int STAGE = (BM + BN) * (ROWB + 4) + (DS * NW > SA + SB ? 256 : 0);
   constexpr int PER_WAVE = DA + DB + DS;   // DMA instructions per wave per K tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  // operand stages, or the staging of the dgrad-of-W2 epilogue when larger
+  constexpr int EPI_LDS = KIND == KIND_DGRAD2 ? gg::dgrad2_mx8_lds_bytes<C>() : 0;
+  constexpr int LDS_BYTES = S * STAGE > EPI_LDS ? S * STAGE : EPI_LDS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -200,11 +209,19 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     if (g < SA) {
       os[j] = a_src_row(64 * g + lane) * (uint32_t)(lda / 32) + (uint32_t)(kp0 / 32);
       os_b[j] = false;
-    } else {
+    } else if (g < SA + SB) {
       os[j] = b_src_row(64 * (g - SA) + lane) * (uint32_t)(ldb / 32) + (uint32_t)(kp0 / 32);
+      os_b[j] = true;
+    } else {
+      os[j] = OOB;                       // spare: zeros into the pad block
       os_b[j] = true;
     }
   }
+  // LDS byte offset (in a stage) of scale DMA j of this wave
+  auto sc_dst = [&](int j) __attribute__((always_inline)) -> uint32_t {
+    const int g = w_uni + NW * j;
+    return g < SA ? (uint32_t)(A_SC + g * 256) : g < SA + SB ? (uint32_t)(B_SC + (g - SA) * 256) : (uint32_t)PAD;
+  };
 
   const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)smem;
   auto issue_tile = [&](int kt, int st) __attribute__((always_inline)) {
@@ -219,10 +236,26 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
       dma16(rcb, live ? ob[i] + kb : OOB, __builtin_amdgcn_readfirstlane(sbase + B_CODES + (i * NW + w_uni) * 1024));
 #pragma unroll
     for (int j = 0; j < DS; ++j) {
-      const int g = w_uni + NW * j;
-      const uint32_t off = live ? os[j] + (uint32_t)kt * 4 : OOB;
-      if (os_b[j]) dma4(rsb, off, __builtin_amdgcn_readfirstlane(sbase + B_SC + (g - SA) * 256));
-      else dma4(rsa, off, __builtin_amdgcn_readfirstlane(sbase + A_SC + g * 256));
+      const uint32_t off = (live && os[j] != OOB) ? os[j] + (uint32_t)kt * 4 : OOB;
+      dma4(os_b[j] ? rsb : rsa, off, __builtin_amdgcn_readfirstlane(sbase + sc_dst(j)));
+    }
+  };
+
+  // DMA instruction q (< PER_WAVE) of this wave for K tile kt into stage st:
+  // A codes, then B codes, then scales
+  auto issue_q = [&](int kt, int st, int q) __attribute__((always_inline)) {
+    const bool live = kt < nk;
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE);
+    const uint32_t kb = (uint32_t)kt * KT;
+    if (q < DA) {
+      dma16(rca, live ? oa[q] + kb : OOB, __builtin_amdgcn_readfirstlane(sbase + A_CODES + (q * NW + w_uni) * 1024));
+    } else if (q < DA + DB) {
+      const int i = q - DA;
+      dma16(rcb, live ? ob[i] + kb : OOB, __builtin_amdgcn_readfirstlane(sbase + B_CODES + (i * NW + w_uni) * 1024));
+    } else {
+      const int j = q - DA - DB;
+      const uint32_t off = (live && os[j] != OOB) ? os[j] + (uint32_t)kt * 4 : OOB;
+      dma4(os_b[j] ? rsb : rsa, off, __builtin_amdgcn_readfirstlane(sbase + sc_dst(j)));
     }
   };
 
@@ -231,6 +264,96 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // a wave whose rows all lie past the expert's end (the ragged last tile)
+  // keeps its share of the DMA and the barriers and skips its fragment reads
+  // and MFMAs: its accumulators stay zero, which the epilogues read as the
+  // zero rows of the padded tile
+  const bool idle = MxKind<KIND>::ragged_rows &&
+                    __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
+  if constexpr (C::PIPE) {
+    // Software pipeline over the wave's 16-row blocks of A (one K tile = one
+    // scaled-MFMA step).  All FN fragments of B stay in registers for the
+    // tile; the A fragment of row block i is read two blocks ahead (four
+    // rotating registers).  One barrier per K tile, at the start of row block
+    // FM-2: every read of this tile's stage is then complete and the DMA of
+    // tile kt+1 has landed, so the stage receives tile kt+S over the last two
+    // row blocks, whose MFMAs also overlap the reads of the next tile: its
+    // first two A fragments, and B fragment j right after its last use here.
+    static_assert(FM % 4 == 0 || FM == 2, "rotating A registers");
+    constexpr int NA = FM >= 4 ? 4 : 2;
+    i32x8_t ar[NA], br[FN];
+    int sa[NA], sb[FN];
+    auto read_a = [&](int st, int i, int slot) __attribute__((always_inline)) {
+      const uint8_t* base = smem + st * STAGE;
+      ar[slot] = frag_codes(base + A_CODES, wm * WM + 16 * i, lane);
+      sa[slot] = frag_scale(base + A_SC, wm * WM + 16 * i, lane);
+    };
+    auto read_b = [&](int st, int j) __attribute__((always_inline)) {
+      const uint8_t* base = smem + st * STAGE;
+      br[j] = frag_codes(base + B_CODES, brow(j), lane);
+      sb[j] = frag_scale(base + B_SC, brow(j), lane);
+    };
+    auto lds_wait_all = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xC07F); };
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+      for (int q = 0; q < PER_WAVE; ++q) issue_q(st, st, q);
+    vm_wait<(S - 1) * PER_WAVE>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int st_c = 0;
+    if (idle) {
+      for (int kt = 0; kt < nk; ++kt) {
+        vm_wait<(S - 2) * PER_WAVE>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < PER_WAVE; ++q) issue_q(kt + S, st_c, q);
+        st_c = (st_c + 1 == S) ? 0 : st_c + 1;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) read_b(0, j);
+      read_a(0, 0, 0);
+      read_a(0, 1, 1);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int st_n = (st_c + 1 == S) ? 0 : st_c + 1;
+        constexpr int NB_LAST = 2 * FN;                            // MFMAs of the last two row blocks
+        constexpr int SP = NB_LAST / PER_WAVE > 0 ? NB_LAST / PER_WAVE : 1;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int slot = i % NA;
+          if (i == FM - 2) {                                       // publish tile kt+1, free this stage
+            lds_wait_all();
+            vm_wait<(S - 2) * PER_WAVE>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+          }
+          // the A fragment two row blocks ahead (of the next tile past FM-2)
+          if (i + 2 < FM) read_a(st_c, i + 2, (i + 2) % NA);
+          else read_a(st_n, i + 2 - FM, (i + 2) % NA);
+          __builtin_amdgcn_sched_barrier(0);                        // issued before this row's MFMAs
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(br[j], ar[slot], acc[i][j], 0, 0, 0, sb[j],
+                                                                         0, sa[slot]);
+            if (i == FM - 1) read_b(st_n, j);                      // B fragment j of the next tile
+            if (i >= FM - 2) {
+              const int idx = (i - (FM - 2)) * FN + j;
+              if (idx % SP == SP - 1 && idx / SP < PER_WAVE) {
+                issue_q(kt + S, st_c, idx / SP);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int q = NB_LAST / SP; q < PER_WAVE; ++q) issue_q(kt + S, st_c, q);
+        st_c = st_n;
+      }
+    }
+  } else {
 
   i32x8_t af[FM], bfr[FN];
   int as[FM], bs[FN];
@@ -260,12 +383,6 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
 #pragma unroll
   for (int st = 0; st < S; ++st) issue_tile(st, st);
   int st_c = 0;
-  // a wave whose rows all lie past the expert's end (the ragged last tile)
-  // keeps its share of the DMA and the barriers and skips its fragment reads
-  // and MFMAs: its accumulators stay zero, which the epilogues read as the
-  // zero rows of the padded tile
-  const bool idle = MxKind<KIND>::ragged_rows &&
-                    __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
   if (idle) {
     for (int kt = 0; kt < nk; ++kt) {
       vm_wait<(S - 1) * PER_WAVE>();
@@ -289,25 +406,34 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
       st_c = (st_c + 1 == S) ? 0 : st_c + 1;
     }
   }
+  }
   vm_wait<0>();      // no DMA may land while the epilogue reuses LDS
   __syncthreads();
 
   if constexpr (KIND == KIND_DGRAD2)
-    gg::dgrad2_epilogue_mx8<C>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
+    gg::dgrad2_epilogue_mx8<C, LDS_BYTES>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
   else
     gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout, wacc);
 }
 
-// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages).  The
-// BK of TileCfg is 64: its bf16 byte count per row (128) is the MXFP8 K tile.
+// Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, tile
+// group divisor, main loop).  The BK of TileCfg is 64: its bf16 byte count
+// per row (128) is the MXFP8 K tile.  Forward kinds: 256 x 256 tiles, 8
+// waves, tile groups of 8 blocks (GEMM W13 13 % and GEMM W2 5 % faster than
+// 128 x 128: half the operand bytes per flop).  Weight gradients: 256 x 256
+// tiles on 4 waves of 128 x 128 with the software-pipelined loop (one wave
+// per SIMD, 4-5 % faster than 8 waves with the two-barrier loop).  The dgrad
+// kinds stay at 128 x 128 (the dgrad-of-W2 epilogue writes one padded
+// 128-token K tile of the weight-gradient operands per tile; 128 x 256 with
+// 4 or 8 waves measured slower).
 #ifndef MOE_MX8_CFG_ROW
 #define MOE_MX8_CFG_ROW 128, 128, 2, 2, 2, 2, 64
 #endif
 #ifndef MOE_MX8_CFG_WGRAD
-#define MOE_MX8_CFG_WGRAD 256, 256, 2, 4, 2, 2, 64
+#define MOE_MX8_CFG_WGRAD 256, 256, 2, 2, 1, 2, 64, 1, 1
 #endif
 #ifndef MOE_MX8_CFG_ROW_FWD
-#define MOE_MX8_CFG_ROW_FWD 128, 128, 2, 2, 2, 2, 64
+#define MOE_MX8_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64, 4
 #endif
 using CfgRowF = TileCfg<MOE_MX8_CFG_ROW_FWD>;   // forward kinds (their own tile table)
 using CfgRow = TileCfg<MOE_MX8_CFG_ROW>;
