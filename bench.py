@@ -412,6 +412,17 @@ def time_extra(g, mi, cfg, mode, base, K, W, ev):
     other = {n: v["ms"] for n, v in res["kernels"].items() if n not in res["_flops"] and v["ms"] >= 0.02}
     if other:
         out["other_kernels_ms"] = other
+    if d.run_mode in ("fp8_bwd", "mxfp8"):
+        # cached MXFP8 weights: quantised once per optimizer step, then every
+        # forward and backward of that step (micro-batches, the checkpointing
+        # recompute) reads the copies
+        qw = time_call(lambda: layer.quantize_weights(w13, w2), K, W)
+        fc = time_call(lambda: layer.forward_cached(x, w13, w2), K, W)
+        bc = time_call(lambda: layer.backward_cached(dy, x), K, W)
+        out["cached_weights"] = {"quantize_weights_ms": qw, "fwd_ms": fc, "bwd_ms": bc,
+                                 "route_fwd_bwd_ms": round(res["route_ms"] + fc + bc, 4),
+                                 "note": "forward and backward reading the MXFP8 weight copies made once per "
+                                         "optimizer step by moe_quantize_weights (timed on its own)"}
     del layer, x, w13, w2, dy, logits
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -8,6 +8,9 @@ Names follow the C ABI in include/moe.h:
     workspace_size(dims) -> (route_ws, saved, fwd_ws, bwd_ws)
     route(dims, logits, routing, ws)
     route_noalloc(dims, logits, routing)
+    weight_codes_size(dims); quantize_weights(dims, w13, w2, codes)
+    forward_cached(dims, x, w13, w2, codes, routing, y, saved, ws)
+    backward_cached(dims, dy, x, codes, routing, saved, dx, dw13, dw2, dgate, dlogits, ws)
     forward(dims, x, w13, w2, routing, y, saved, ws)
     backward(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws)
     mxfp8_quantize(src, along, codes, scales)
@@ -24,7 +27,8 @@ __all__ = [
     "MODE_FP32", "MODE_BF16", "MODE_MXFP8", "MODE_FP8_BWD", "Dims", "RoutingBuffers",
     "MoeError", "lib_path", "load_library", "workspace_size", "route", "forward", "backward",
     "alloc_routing", "alloc_workspace", "status_str", "MoeLayer", "num_kernels", "mxfp8_quantize",
-    "mxfp8_quantize_grouped", "mxfp8_grouped_capacity", "route_noalloc",
+    "mxfp8_quantize_grouped", "mxfp8_grouped_capacity", "route_noalloc", "weight_codes_size", "quantize_weights",
+    "forward_cached", "backward_cached",
 ]
 
 MODE_FP32, MODE_BF16, MODE_MXFP8, MODE_FP8_BWD = 0, 1, 2, 3
@@ -86,6 +90,16 @@ def load_library():
                                  vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_workspace_size", "moe_route", "moe_forward", "moe_backward"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.moe_weight_codes_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
+    lib.moe_weight_codes_size.restype = ctypes.c_int
+    lib.moe_quantize_weights.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, sz, vp]
+    lib.moe_quantize_weights.restype = ctypes.c_int
+    lib.moe_forward_cached.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, ctypes.POINTER(_CRouting), vp, vp, vp,
+                                       sz, vp]
+    lib.moe_forward_cached.restype = ctypes.c_int
+    lib.moe_backward_cached.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, ctypes.POINTER(_CRouting), vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
+    lib.moe_backward_cached.restype = ctypes.c_int
     lib.moe_route_noalloc.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(_CRouting), vp]
     lib.moe_route_noalloc.restype = ctypes.c_int
     lib.moe_route_project.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, ctypes.POINTER(_CRouting), vp, sz, vp]
@@ -239,6 +253,37 @@ def backward(dims: Dims, dy, x, w13, w2, routing: RoutingBuffers, saved, dx, dw1
         _check(lib.moe_backward_timed(*args, events, len(events)), "moe_backward_timed")
 
 
+def weight_codes_size(dims: Dims) -> int:
+    """Bytes of the MXFP8 weight copies of an fp8 mode (moe_weight_codes_size)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().moe_weight_codes_size(ctypes.byref(dims), ctypes.byref(out)), "moe_weight_codes_size")
+    return out.value
+
+
+def quantize_weights(dims: Dims, w13, w2, codes, stream=None):
+    """MXFP8 copies of the weights into `codes` (uint8 tensor, moe_quantize_weights)."""
+    _check(load_library().moe_quantize_weights(ctypes.byref(dims), _ptr(w13), _ptr(w2), _ptr(codes), codes.numel(),
+                                               _stream(stream)), "moe_quantize_weights")
+
+
+def forward_cached(dims: Dims, x, w13, w2, codes, routing: RoutingBuffers, y, saved, ws, stream=None):
+    """moe_forward_cached: the MXFP8 GEMMs take their weights from `codes`."""
+    r = routing.c()
+    _check(load_library().moe_forward_cached(ctypes.byref(dims), _ptr(x), _ptr(w13), _ptr(w2), _ptr(codes),
+                                             ctypes.byref(r), _ptr(y), _ptr(saved), _ptr(ws), ws.numel(),
+                                             _stream(stream)), "moe_forward_cached")
+
+
+def backward_cached(dims: Dims, dy, x, codes, routing: RoutingBuffers, saved, dx, dw13, dw2, dgate, dlogits, ws,
+                    stream=None):
+    """moe_backward_cached: the MXFP8 GEMMs take their weights from `codes`."""
+    r = routing.c()
+    _check(load_library().moe_backward_cached(ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(codes), ctypes.byref(r),
+                                              _ptr(saved), _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dgate),
+                                              _ptr(dlogits), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_backward_cached")
+
+
 def num_kernels(dims: Dims, which: str) -> int:
     n = load_library().moe_num_kernels(ctypes.byref(dims), {"route": 0, "forward": 1, "backward": 2}[which])
     if n < 0:
@@ -316,6 +361,22 @@ class MoeLayer:
     def forward_recompute(self, x, w13, w2, stream=None):
         """Second forward of activation checkpointing: `saved` as forward() writes it, y untouched."""
         forward_recompute(self.dims, x, w13, w2, self.routing, self.saved, self.fwd_ws, stream)
+
+    def quantize_weights(self, w13, w2, stream=None):
+        """MXFP8 copies of the weights (fp8 modes), kept in self.wcodes for the cached calls."""
+        if getattr(self, "wcodes", None) is None:
+            self.wcodes = alloc_workspace(weight_codes_size(self.dims), self.device)
+        quantize_weights(self.dims, w13, w2, self.wcodes, stream)
+        return self.wcodes
+
+    def forward_cached(self, x, w13, w2, stream=None):
+        forward_cached(self.dims, x, w13, w2, self.wcodes, self.routing, self.y, self.saved, self.fwd_ws, stream)
+        return self.y
+
+    def backward_cached(self, dy, x, want_dlogits=True, stream=None):
+        backward_cached(self.dims, dy, x, self.wcodes, self.routing, self.saved, self.dx, self.dw13, self.dw2,
+                        self.dgate, self.dlogits if want_dlogits else None, self.bwd_ws, stream)
+        return self.dx, self.dw13, self.dw2, self.dgate, (self.dlogits if want_dlogits else None)
 
     def backward(self, dy, x, w13, w2, want_dlogits=True, stream=None, events=None, accumulate=False):
         backward(self.dims, dy, x, w13, w2, self.routing, self.saved, self.dx, self.dw13, self.dw2, self.dgate,

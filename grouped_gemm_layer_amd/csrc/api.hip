@@ -133,6 +133,32 @@ Sizes compute_sizes(const moe_dims* d) {
   return s;
 }
 
+// Layout of the caller's cache of MXFP8 weight copies (moe_quantize_weights):
+// the forward's row-wise copies (MOE_MODE_MXFP8) and the backward's transposed
+// copies (both fp8 modes), codes then scales, each 256-byte aligned.
+struct WCodes {
+  size_t qw13, sw13, qw2, sw2, qw13t, sw13t, qw2t, sw2t, bytes;
+};
+WCodes wcodes_layout(const moe_dims* d) {
+  WCodes w{};
+  const size_t n13 = (size_t)d->E * 2 * d->I * d->H, n2 = (size_t)d->E * d->H * d->I;
+  size_t o = 0;
+  if (mx8_forward(d->mode)) {
+    w.qw13 = o; o += align_up(n13);
+    w.sw13 = o; o += align_up(n13 / 32);
+    w.qw2 = o;  o += align_up(n2);
+    w.sw2 = o;  o += align_up(n2 / 32);
+  }
+  if (mx8_backward(d->mode)) {
+    w.qw13t = o; o += align_up(n13);
+    w.sw13t = o; o += align_up(n13 / 32);
+    w.qw2t = o;  o += align_up(n2);
+    w.sw2t = o;  o += align_up(n2 / 32);
+  }
+  w.bytes = o;
+  return w;
+}
+
 moe_status check_routing(const moe_routing* r) {
   if (!r) return MOE_ERR_NULL;
   if (!r->topk_idx || !r->gate || !r->counts || !r->offsets || !r->sorted_to_flat || !r->flat_to_sorted)
@@ -214,13 +240,15 @@ inline int backward_kernels(int mode) {
          : mode == MOE_MODE_FP32 ? kBackwardKernels : kBackwardKernels + 1;
 }
 
+// wcodes: the caller's MXFP8 weight copies (moe_quantize_weights), or null
+// when the call quantises the weights itself
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
-                        hipStream_t stream, Marks mk, bool recompute = false);
+                        hipStream_t stream, Marks mk, bool recompute = false, const void* wcodes = nullptr);
 moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,
                          const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
                          float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk,
-                         bool accumulate = false);
+                         bool accumulate = false, const void* wcodes = nullptr);
 
 }  // namespace
 
@@ -317,7 +345,7 @@ namespace {
 // `saved` for the backward and skips what only produces y (GEMM W2, combine)
 moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, const void* w2,
                         const moe_routing* routing, void* y, void* saved, void* ws, size_t ws_bytes,
-                        hipStream_t stream, Marks mk, bool recompute) {
+                        hipStream_t stream, Marks mk, bool recompute, const void* wcodes) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_routing(routing)) != MOE_OK) return st;
@@ -354,6 +382,12 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
     q.qa = u8(s.f_qa);     q.sa = u8(s.f_sa);
     if (!recompute) { a.q_a = u8(s.f_qa); a.q_sa = u8(s.f_sa); }
     q.qw2 = u8(s.f_qw2);   q.sw2 = u8(s.f_sw2);
+    if (wcodes) {   // the caller's copies: no weight quantisation in this call
+      const WCodes wc = wcodes_layout(dims);
+      auto cp = [&](size_t off) { return static_cast<const uint8_t*>(wcodes) + off; };
+      q.qw13 = cp(wc.qw13); q.sw13 = cp(wc.sw13);
+      q.qw2 = cp(wc.qw2);   q.sw2 = cp(wc.sw2);
+    }
     const bf16_t* x16 = static_cast<const bf16_t*>(x);
     if (e == hipSuccess) step(launch_mx_quant_rows(x16, a.T, a.H, nullptr, 1, u8(s.f_qx), u8(s.f_sx), stream));
     auto svp = [&](size_t off) { return static_cast<uint8_t*>(saved) + off; };
@@ -366,10 +400,10 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
       else
         step(launch_mx_quant_rows(w16, a.E * rows_per_e, cols, nullptr, 1, u8(f_q), u8(f_s), stream));
     };
-    if (e == hipSuccess) quant_w(w13, 2 * a.I, a.H, s.sv_qw13t, s.sv_sw13t, s.f_qw13, s.f_sw13);
+    if (e == hipSuccess && !wcodes) quant_w(w13, 2 * a.I, a.H, s.sv_qw13t, s.sv_sw13t, s.f_qw13, s.f_sw13);
     if (e == hipSuccess) step(launch_gemm_mx8(KIND_FWD1, a, q, stream));
     // the transposed W2 copy in `saved` is the backward's, so the recompute keeps it
-    if (e == hipSuccess) quant_w(w2, a.H, a.I, s.sv_qw2t, s.sv_sw2t, s.f_qw2, s.f_sw2);
+    if (e == hipSuccess && !wcodes) quant_w(w2, a.H, a.I, s.sv_qw2t, s.sv_sw2t, s.f_qw2, s.f_sw2);
     if (e == hipSuccess && !recompute) step(launch_gemm_mx8(KIND_FWD2, a, q, stream));
   } else {
     if (e == hipSuccess) step(gemm(bf16, KIND_FWD1, a, stream));
@@ -390,11 +424,13 @@ moe_status forward_impl(const moe_dims* dims, const void* x, const void* w13, co
 moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, const void* w13, const void* w2,
                          const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
                          float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream, Marks mk,
-                         bool accumulate) {
+                         bool accumulate, const void* wcodes) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_routing(routing)) != MOE_OK) return st;
-  if (!dy || !x || !w13 || !w2 || !saved || !dx || !dw13 || !dw2 || !dgate || !ws) return MOE_ERR_NULL;
+  // with the caller's weight copies the bf16 weights are not read
+  if (!dy || !x || (!wcodes && (!w13 || !w2)) || !saved || !dx || !dw13 || !dw2 || !dgate || !ws)
+    return MOE_ERR_NULL;
   if (!aligned(dy) || !aligned(x) || !aligned(w13) || !aligned(w2) || !aligned(saved) || !aligned(dx) ||
       !aligned(dw13) || !aligned(dw2) || !aligned(dgate) || !aligned(ws) || (dlogits && !aligned(dlogits)))
     return MOE_ERR_ALIGN;
@@ -428,7 +464,13 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     a.wpart2 = reinterpret_cast<float*>(at(ws, s.b_wpart2));
   }
   const int bm = bwd_row_tile_m(dims->mode);
-  const Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
+  Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
+  if (mx8 && wcodes) {   // the caller's transposed weight copies
+    const WCodes wc = wcodes_layout(dims);
+    auto cp = [&](size_t off) { return static_cast<const uint8_t*>(wcodes) + off; };
+    q.qw2t = cp(wc.qw2t);   q.sw2t = cp(wc.sw2t);
+    q.qw13t = cp(wc.qw13t); q.sw13t = cp(wc.sw13t);
+  }
   const bf16_t* dy16 = static_cast<const bf16_t*>(dy);
   const bf16_t* x16 = static_cast<const bf16_t*>(x);
   // activation-gradient chain first; the weight gradients do not feed it
@@ -441,7 +483,8 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
   if (mx8) {
     // the dgrad epilogue of W2 places its token blocks at the padded offsets
     if (e == hipSuccess) step(launch_pad_offsets(a.offsets, a.E, const_cast<int32_t*>(q.pad_off), stream));
-    const bool wq = !mx8_forward(dims->mode);   // mxfp8: the forward saved W2^T and W13^T codes
+    // mxfp8: the forward saved W2^T and W13^T codes; cached: the caller's copies
+    const bool wq = !mx8_forward(dims->mode) && !wcodes;
     if (e == hipSuccess && wq)
       step(launch_mx_quant_cols_t(static_cast<const bf16_t*>(w2), a.E, a.H, a.I, mut(q.qw2t), mut(q.sw2t), stream));
     if (e == hipSuccess) step(launch_mx_quant_rows(dy16, a.T, a.H, nullptr, 1, mut(q.qdy), mut(q.sdy), stream));
@@ -537,6 +580,64 @@ moe_status moe_backward_timed(const moe_dims* dims, const void* dy, const void* 
   if (check_dims(dims) == MOE_OK && n_events < backward_kernels(dims->mode) + 1) return MOE_ERR_DIMS;
   return backward_impl(dims, dy, x, w13, w2, routing, saved, dx, dw13, dw2, dgate, dlogits, ws, ws_bytes, stream,
                        Marks{events, n_events, 0, stream});
+}
+
+moe_status moe_weight_codes_size(const moe_dims* dims, size_t* bytes) {
+  const moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  if (!mx8_backward(dims->mode)) return MOE_ERR_UNSUPPORTED;
+  *bytes = wcodes_layout(dims).bytes;
+  return MOE_OK;
+}
+
+moe_status moe_quantize_weights(const moe_dims* dims, const void* w13, const void* w2, void* codes, size_t bytes,
+                                hipStream_t stream) {
+  const moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!mx8_backward(dims->mode)) return MOE_ERR_UNSUPPORTED;
+  if (!w13 || !w2 || !codes) return MOE_ERR_NULL;
+  if (!aligned(w13) || !aligned(w2) || !aligned(codes)) return MOE_ERR_ALIGN;
+  const WCodes wc = wcodes_layout(dims);
+  if (bytes < wc.bytes) return MOE_ERR_WORKSPACE;
+  auto cp = [&](size_t off) { return static_cast<uint8_t*>(codes) + off; };
+  const bf16_t* w13_16 = static_cast<const bf16_t*>(w13);
+  const bf16_t* w2_16 = static_cast<const bf16_t*>(w2);
+  const int E = dims->E, H = dims->H, I = dims->I;
+  hipError_t e;
+  if (mx8_forward(dims->mode)) {   // both copies of each weight from one read
+    e = launch_mx_quant_both(w13_16, E, 2 * I, H, cp(wc.qw13t), cp(wc.sw13t), cp(wc.qw13), cp(wc.sw13), stream);
+    if (e == hipSuccess)
+      e = launch_mx_quant_both(w2_16, E, H, I, cp(wc.qw2t), cp(wc.sw2t), cp(wc.qw2), cp(wc.sw2), stream);
+  } else {                         // fp8_bwd: the backward's transposed copies only
+    e = launch_mx_quant_cols_t(w13_16, E, 2 * I, H, cp(wc.qw13t), cp(wc.sw13t), stream);
+    if (e == hipSuccess) e = launch_mx_quant_cols_t(w2_16, E, H, I, cp(wc.qw2t), cp(wc.sw2t), stream);
+  }
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+moe_status moe_forward_cached(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                              const void* codes, const moe_routing* routing, void* y, void* saved, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!mx8_backward(dims->mode)) return MOE_ERR_UNSUPPORTED;
+  if (!codes) return MOE_ERR_NULL;
+  if (!aligned(codes)) return MOE_ERR_ALIGN;
+  return forward_impl(dims, x, w13, w2, routing, y, saved, ws, ws_bytes, stream, Marks{nullptr, 0, 0, stream}, false,
+                      codes);
+}
+
+moe_status moe_backward_cached(const moe_dims* dims, const void* dy, const void* x, const void* codes,
+                               const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
+                               float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!mx8_backward(dims->mode)) return MOE_ERR_UNSUPPORTED;
+  if (!codes) return MOE_ERR_NULL;
+  if (!aligned(codes)) return MOE_ERR_ALIGN;
+  return backward_impl(dims, dy, x, nullptr, nullptr, routing, saved, dx, dw13, dw2, dgate, dlogits, ws, ws_bytes,
+                       stream, Marks{nullptr, 0, 0, stream}, false, codes);
 }
 
 moe_status moe_mxfp8_quantize(const void* src, int32_t rows, int32_t cols, int32_t along, uint8_t* codes,

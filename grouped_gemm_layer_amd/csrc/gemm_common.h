@@ -60,8 +60,12 @@ __device__ __forceinline__ bool decode_row_tile(const LayerArgs& a, int L, int n
   return true;
 }
 
-template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64, int GD_ = 1, int PIPE_ = 0>
+template <int BM_, int BN_, int WGM_, int WGN_, int WPE_, int ST_, int BK_ = 64, int GD_ = 1, int PIPE_ = 0,
+          int PERSIST_ = 0>
 struct TileCfg {
+  // grid: 0 = one block per tile; 1 = persistent, the resident blocks loop
+  // over the tiles in the same order
+  static constexpr int PERSIST = PERSIST_;
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
   // main loop: 0 = every wave reads a whole K tile's fragments between two
   // barriers, then runs its MFMAs; 1 = software pipeline, the fragments of the

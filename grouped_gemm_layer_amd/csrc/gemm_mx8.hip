@@ -81,7 +81,7 @@ template <int KIND> struct MxKind {
 
 template <int KIND, class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::WPE)))
-void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
+void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total, int nvb) {
   constexpr int BM = C::BM, BN = C::BN, NTHR = C::NTHR, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int NW = C::NW, S = C::STAGES;
   constexpr int DA = BM * ROWB / 1024 / NW, DB = BN * ROWB / 1024 / NW;   // 1 KiB code DMAs per wave
@@ -101,18 +101,27 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   constexpr int LDS_BYTES = S * STAGE > EPI_LDS ? S * STAGE : EPI_LDS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // The block takes the virtual blocks vb = blockIdx.x, blockIdx.x + gridDim.x,
+  // ... below nvb (one when the grid covers them all; a persistent block
+  // otherwise)
+  auto tile_body = [&](const int vb) __attribute__((always_inline)) {
+  // the thread index passes through an empty asm statement, so that nothing
+  // derived from it is hoisted out of a persistent block's tile loop (that
+  // would keep per-lane addresses live across the epilogue)
+  int tid = threadIdx.x;
+  if constexpr (C::PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int H = a.H, I = a.I, k = a.k;
-
   // ---------------- tile decode (row kinds: XCD-contiguous renumbering of the
   // tile table; weight gradients: experts by decreasing size, see decode_wgrad_tile)
   int e, m0, mlim, n0, nk, kp0 = 0;
   float* wout = nullptr;   // weight gradients: dW[e], or the chunk's partial slot
   bool wacc = false;       //   dW[e] adds the caller's value (accumulate-into)
   if constexpr (MxKind<KIND>::ragged_rows) {
-    const int per_xcd = gridDim.x / NXCD;
-    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+    const int per_xcd = nvb / NXCD;
+    const int L = (vb % NXCD) * per_xcd + vb / NXCD;
     if (L >= tiles_total) return;
     gg::RowTile rt;
     if (!gg::decode_row_tile(a, L, n_tiles, C::GROUP, rt)) return;
@@ -124,7 +133,7 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
   } else {
     const int per_e = n_tiles * (((KIND == KIND_WGRAD2 ? H : 2 * I) + BM - 1) / BM);
     int t, r0, r1, slot;
-    if (!decode_wgrad_tile(a, per_e, e, r0, r1, slot, t)) return;
+    if (!decode_wgrad_tile(a, vb, per_e, e, r0, r1, slot, t)) return;
     m0 = (t / n_tiles) * BM;
     n0 = (t % n_tiles) * BN;
     kp0 = q.pad_off[e] + r0;              // chunks start on K-tile boundaries of the padded rows
@@ -414,6 +423,15 @@ void gemm_mx8_kernel(LayerArgs a, Mx8Args q, int n_tiles, int tiles_total) {
     gg::dgrad2_epilogue_mx8<C, LDS_BYTES>(a, q, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0);
   else
     gg::gemm_epilogue<KIND, C, true>(a, acc, smem, tid, lane, wm, wn, e, m0, mlim, n0, nlim, wout, wacc);
+  };
+  if constexpr (C::PERSIST) {
+    for (int vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+      tile_body(vb);
+      __syncthreads();   // every wave is done with the LDS before the next tile's DMA lands
+    }
+  } else {
+    tile_body(blockIdx.x);
+  }
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, tile
@@ -453,9 +471,10 @@ hipError_t launch_kind(const LayerArgs& a, const Mx8Args& q, hipStream_t s) {
     n_tiles = (ndim + C::BN - 1) / C::BN;
     tiles = a.E * n_tiles * ((mdim + C::BM - 1) / C::BM);
   }
-  const int grid = MxKind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
-                                             : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
-  return launch_kernel((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles);
+  const int nvb = MxKind<KIND>::ragged_rows ? (tiles + NXCD - 1) / NXCD * NXCD
+                                            : wgrad_grid(wgrad_max_chunks(a.M, a.E), tiles / a.E);
+  const int grid = C::PERSIST ? min(nvb, resident_blocks(C::WPE * 4 / C::NW)) : nvb;
+  return launch_kernel((gemm_mx8_kernel<KIND, C>), dim3(grid), dim3(C::NTHR), 0, s, a, q, n_tiles, tiles, nvb);
 }
 
 }  // namespace

@@ -178,7 +178,10 @@ hipError_t route_scratch_ptr(void** ptr);
 // Rows per weight-gradient chunk: an expert with more rows is split along K
 // (its rows) into chunks of WG_KC rows (a multiple of the 128-row MXFP8 K tile
 // and of every bf16 K tile), whose fp32 results are summed in chunk order.
-constexpr int WG_KC = 4096;
+#ifndef MOE_WG_KC
+#define MOE_WG_KC 4096
+#endif
+constexpr int WG_KC = MOE_WG_KC;
 struct WgradList {              // device tables written by the backward's tile-table kernel
   int32_t* order;               // [E]   expert of each rank, by decreasing row count (ties: index)
   int32_t* cstart;              // [E+1] first chunk of each rank (exclusive prefix of the chunk counts)
@@ -246,8 +249,8 @@ constexpr int FP32_BN = 64;
 // mode: 0 fp32, 1 bf16, 2 mxfp8, 3 fp8_bwd (the public moe_mode values)
 inline bool mx8_forward(int mode) { return mode == 2; }
 inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
-// Weight-gradient tile of this block: block b goes to XCD b % 8 (round-robin
-// dispatch); in round q the XCDs take chunks 8q .. 8q + 7 of the work list
+// Weight-gradient tile of virtual block vb (the block index of a grid with
+// one block per tile): block b goes to XCD b % 8 (round-robin dispatch); in round q the XCDs take chunks 8q .. 8q + 7 of the work list
 // (experts by decreasing row count, an expert's chunks consecutive), XCD x
 // chunk 8q + x in even rounds and 8q + 7 - x in odd ones (a snake, so that no
 // XCD always draws the longest chunk of a round), each as per_e consecutive
@@ -255,9 +258,9 @@ inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
 // start first and the load of the XCDs stays even.
 // Gives the expert e, its rows [r0, r1) (expert-local), the partial slot (-1
 // for chunk 0, which writes dW[e]) and the tile t; false past the last chunk.
-__device__ __forceinline__ bool decode_wgrad_tile(const LayerArgs& a, int per_e, int& e, int& r0, int& r1,
+__device__ __forceinline__ bool decode_wgrad_tile(const LayerArgs& a, int vb, int per_e, int& e, int& r0, int& r1,
                                                   int& slot, int& t) {
-  const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+  const int x = vb % 8, j = vb / 8;
   const int q = j / per_e;
   const int item = 8 * q + ((q & 1) ? 7 - x : x);
   if (item >= a.wg_cstart[a.E]) return false;
@@ -276,6 +279,10 @@ __device__ __forceinline__ bool decode_wgrad_tile(const LayerArgs& a, int per_e,
   return true;
 }
 inline int wgrad_grid(int max_chunks, int per_e) { return 8 * ((max_chunks + 7) / 8) * per_e; }
+// Blocks of a persistent GEMM grid: per_cu resident blocks on every compute
+// unit of the current device, a multiple of the 8 XCDs (block b runs on XCD
+// b % 8, so a block keeps its XCD from one virtual block to the next).
+int resident_blocks(int per_cu);
 
 inline int fwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_fwd_row_tile_m() : bf16_fwd_row_tile_m();

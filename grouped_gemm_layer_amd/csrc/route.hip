@@ -244,6 +244,21 @@ hipError_t route_scratch_ptr(void** ptr) {
   return hipSuccess;
 }
 
+int resident_blocks(int per_cu) {
+  constexpr int kMaxDevices = 64;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  int n = dev >= 0 ? __atomic_load_n(&cus[dev], __ATOMIC_RELAXED) : 0;
+  if (n == 0) {
+    if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    if (dev >= 0) __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
+  }
+  const int b = n * (per_cu > 0 ? per_cu : 1);
+  return b < 8 ? 8 : b / 8 * 8;
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* gate,
                         int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
                         int32_t* ws_partials, int32_t* ws_bases, hipStream_t s) {

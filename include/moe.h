@@ -237,6 +237,41 @@ moe_status moe_backward_accumulate(const moe_dims* dims, const void* dy, const v
                                    void* dx, float* dw13, float* dw2, float* dgate, float* dlogits,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Cached MXFP8 weights, for the two fp8 modes (Prime Mega MoE news page,
+ * "How does the fused kernel work?": MXFP8 and fp8_bwd precisions; the
+ * weights change once per optimizer step, while a training step runs the
+ * forward twice under activation checkpointing and every micro-batch reuses
+ * them, so their MXFP8 copies can be made once and kept by the caller).
+ *   moe_weight_codes_size: bytes of the copies the mode uses (host-only):
+ *     MOE_MODE_MXFP8: W13 along H and W2 along I (the forward's operands) and
+ *       W13^T along 2I and W2^T along H (the backward's);
+ *     MOE_MODE_FP8_BWD: W13^T and W2^T.
+ *     Codes then scales per copy, each as moe_mxfp8_quantize writes them
+ *     (along = 1 for the row-wise copies of the [E*2I, H] and [E*H, I]
+ *     weights, along = 0 per expert for the transposed ones), each 256-byte
+ *     aligned, in the order listed.  MOE_ERR_UNSUPPORTED in the other modes.
+ *   moe_quantize_weights: writes them from w13, w2 (device bf16, as for
+ *     moe_forward; each weight read once); codes: device buffer of at least
+ *     that size (MOE_ERR_WORKSPACE otherwise), owned by the caller.
+ *   moe_forward_cached / moe_backward_cached: moe_forward / moe_backward with
+ *     the weight operands of the MXFP8 GEMMs taken from `codes` instead of
+ *     quantised in the call.  Results are bit for bit those of moe_forward /
+ *     moe_backward on the weights the codes were made from.  w13, w2: the
+ *     bf16 weights, read by the bf16 forward GEMMs of MOE_MODE_FP8_BWD (in
+ *     MOE_MODE_MXFP8 they are not read); the backward reads no bf16 weight.
+ *     In MOE_MODE_MXFP8 the `saved` of moe_forward_cached holds G13 only, so
+ *     its backward must be moe_backward_cached with the same codes.  Other
+ *     arguments, sizes and errors as for moe_forward / moe_backward. */
+moe_status moe_weight_codes_size(const moe_dims* dims, size_t* bytes);
+moe_status moe_quantize_weights(const moe_dims* dims, const void* w13, const void* w2, void* codes, size_t bytes,
+                                hipStream_t stream);
+moe_status moe_forward_cached(const moe_dims* dims, const void* x, const void* w13, const void* w2,
+                              const void* codes, const moe_routing* routing, void* y, void* saved, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+moe_status moe_backward_cached(const moe_dims* dims, const void* dy, const void* x, const void* codes,
+                               const moe_routing* routing, const void* saved, void* dx, float* dw13, float* dw2,
+                               float* dgate, float* dlogits, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Benchmarking variants of moe_forward / moe_backward: the same work, and in
  * addition events[0] is recorded on `stream` before the first kernel and
  * events[i+1] after kernel i, so that hipEventElapsedTime(events[i],

@@ -284,3 +284,42 @@ def test_route_noalloc_limit_checked_before_launch():
     assert lib.moe_route_noalloc(ctypes.byref(ok), ctypes.c_void_p(0x7E0000000004), ctypes.byref(c), None) == 4
     assert lib.moe_route_noalloc(ctypes.byref(g.Dims.of(64, 128, 64, 8, 9, "bf16")), logits, ctypes.byref(c),
                                  None) == 2
+
+
+def test_weight_codes_sizes_and_errors():
+    """moe_weight_codes_size: two transposed copies in fp8_bwd, four copies in
+    mxfp8, unsupported without MXFP8 GEMMs; the cached calls validate before
+    any launch."""
+    g, lib = _lib()
+    T, H, I, E, k = 64, 256, 128, 8, 2
+    al = lambda n: (n + 255) // 256 * 256
+    one = al(E * 2 * I * H) + al(E * 2 * I * H // 32) + al(E * H * I) + al(E * H * I // 32)
+    assert g.weight_codes_size(g.Dims.of(T, H, I, E, k, "fp8_bwd")) == one
+    assert g.weight_codes_size(g.Dims.of(T, H, I, E, k, "mxfp8")) == 2 * one
+    sz = ctypes.c_size_t(0)
+    assert lib.moe_weight_codes_size(ctypes.byref(g.Dims.of(T, H, I, E, k, "bf16")), ctypes.byref(sz)) == 3
+    assert lib.moe_weight_codes_size(ctypes.byref(g.Dims.of(T, H, I, E, k, "mxfp8")), None) == 1
+    t = lambda i: ctypes.c_void_p(0x7C0000000000 + i * 0x1000000)
+    d8 = g.Dims.of(T, H, I, E, k, "fp8_bwd")
+    q = lib.moe_quantize_weights
+    assert q(ctypes.byref(g.Dims.of(T, H, I, E, k, "bf16")), t(0), t(1), t(2), 1 << 30, None) == 3
+    assert q(ctypes.byref(d8), None, t(1), t(2), 1 << 30, None) == 1
+    assert q(ctypes.byref(d8), t(0), t(1), ctypes.c_void_p(0x7C0000000010), 1 << 30, None) == 4
+    assert q(ctypes.byref(d8), t(0), t(1), t(2), one - 1, None) == 5
+    r = _fake_routing(g)
+    c = r.c()
+    fc, bc = lib.moe_forward_cached, lib.moe_backward_cached
+    # forward_cached(dims, x, w13, w2, codes, routing, y, saved, ws, ws_bytes, stream)
+    assert fc(ctypes.byref(g.Dims.of(T, H, I, E, k, "bf16")), t(0), t(1), t(2), t(3), ctypes.byref(c), t(4), t(5),
+              t(6), 1 << 30, None) == 3
+    assert fc(ctypes.byref(d8), t(0), t(1), t(2), None, ctypes.byref(c), t(4), t(5), t(6), 1 << 30, None) == 1
+    assert fc(ctypes.byref(d8), t(0), t(1), t(2), ctypes.c_void_p(0x7C0000000010), ctypes.byref(c), t(4), t(5),
+              t(6), 1 << 30, None) == 4
+    assert fc(ctypes.byref(d8), t(0), t(1), t(2), t(3), ctypes.byref(c), t(4), t(5), t(6), 16, None) == 5
+    # backward_cached(dims, dy, x, codes, routing, saved, dx, dw13, dw2, dgate, dlogits, ws, ws_bytes, stream)
+    assert bc(ctypes.byref(d8), t(0), t(1), None, ctypes.byref(c), t(4), t(5), t(6), t(7), t(8), None, t(9),
+              1 << 30, None) == 1
+    assert bc(ctypes.byref(d8), t(0), t(1), t(3), ctypes.byref(c), t(4), t(5), t(6), t(7), t(8), None, t(9),
+              16, None) == 5
+    assert bc(ctypes.byref(g.Dims.of(T, H, I, E, k, "bf16")), t(0), t(1), t(3), ctypes.byref(c), t(4), t(5), t(6),
+              t(7), t(8), None, t(9), 1 << 30, None) == 3
