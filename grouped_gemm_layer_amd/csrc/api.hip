@@ -24,7 +24,7 @@ struct Sizes {
   size_t r_partials, r_bases;
   size_t f_tile_e, f_tile_r, f_tile_x, f_A, f_O;
   size_t f_qx, f_sx, f_qw13, f_sw13, f_qa, f_sa, f_qw2, f_sw2;   // mxfp8 forward operands
-  size_t b_tile_e, b_tile_r, b_tile_x, b_wg_order, b_wg_cstart, b_wg_slot0, b_wpart13, b_wpart2;
+  size_t b_tile_e, b_tile_r, b_tile_x, b_wg_order, b_wg_cstart, b_wg_slot0, b_wg_xq, b_wpart13, b_wpart2;
   size_t b_dG13, b_Ag, b_dXp, b_part;
   // fp8_bwd: MXFP8 operand copies of the backward GEMMs (codes, scales)
   size_t Mp;
@@ -101,6 +101,7 @@ Sizes compute_sizes(const moe_dims* d) {
   s.b_wg_order = o;  o += align_up((size_t)d->E * 4);
   s.b_wg_cstart = o; o += align_up(((size_t)d->E + 1) * 4);
   s.b_wg_slot0 = o;  o += align_up((size_t)d->E * 4);
+  s.b_wg_xq = o;     o += align_up((size_t)wgrad_queue_slots(wgrad_max_chunks((int)M, d->E)) * 4);
   if (d->mode != MOE_MODE_FP32) {   // fp32 partial results of the chunks c > 0 of split experts
     const size_t slots = wgrad_max_slots(M);
     s.b_wpart13 = o; o += align_up(slots * 2 * d->I * d->H * 4);
@@ -459,7 +460,8 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     wg.order = reinterpret_cast<int32_t*>(at(ws, s.b_wg_order));
     wg.cstart = reinterpret_cast<int32_t*>(at(ws, s.b_wg_cstart));
     wg.slot0 = reinterpret_cast<int32_t*>(at(ws, s.b_wg_slot0));
-    a.wg_order = wg.order; a.wg_cstart = wg.cstart; a.wg_slot0 = wg.slot0;
+    wg.xq = reinterpret_cast<int32_t*>(at(ws, s.b_wg_xq));
+    a.wg_order = wg.order; a.wg_cstart = wg.cstart; a.wg_slot0 = wg.slot0; a.wg_xq = wg.xq;
     a.wpart13 = reinterpret_cast<float*>(at(ws, s.b_wpart13));
     a.wpart2 = reinterpret_cast<float*>(at(ws, s.b_wpart2));
   }

@@ -563,14 +563,16 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
 #endif
+// Weight gradients: two 4-wave blocks per CU (57 KB of LDS each), so that
+// one block's fp32 output stores overlap the other's main loop.  wgrad of W2
+// (M = H, N = I): 128 x 256, wgrad of W13 (M = 2I, N = H): 256 x 128; against
+// one 8-wave 256 x 256 block per CU, 1-2 % and 3 % faster with the even
+// routing, 4 % and 7 % with the skewed one.
 #ifndef MOE_CFG_WGRAD
-#define MOE_CFG_WGRAD 256, 256, 2, 4, 2, 2, 32
+#define MOE_CFG_WGRAD 128, 256, 2, 2, 2, 2, 32
 #endif
-// wgrad of W13 (K = expert rows, M = 2I, N = H): K tile 64 with the
-// software-pipelined loop (3 % faster; the same for the wgrad of W2 was 5 %
-// slower)
 #ifndef MOE_CFG_WGRAD1
-#define MOE_CFG_WGRAD1 256, 256, 2, 4, 2, 2, 64, 1, 1
+#define MOE_CFG_WGRAD1 256, 128, 2, 2, 2, 2, 32
 #endif
 using CfgRowF = TileCfg<MOE_CFG_ROW_FWD>;
 using CfgRow = TileCfg<MOE_CFG_ROW>;

@@ -600,11 +600,17 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
           }
         }
       }
-      // row blocks of dG13 (32 columns = fragments 2jp, 2jp+1; 4 lanes per row)
+      // row blocks of dG13 (32 columns = fragments 2jp, 2jp+1).  The 4 lanes
+      // sharing a row (lane groups g = lane/16) hold codes of the 4 blocks
+      // b = 2 ii + h of that row pair: group g has dwords g and 4 + g (columns
+      // 4g.., 16 + 4g..) of each.  A 4x4 transpose over the groups (a 32-lane
+      // then a 16-lane row swap) gives group g all 8 dwords of block g, stored
+      // as two 16-byte pieces with the block's scale byte.
       const int c0 = n0 + wn * WN + 32 * jp;
+      uint32_t pk[4][2];   // [block b][jj]: before the transpose, dword g (+4 jj) of block b
+      int xs[4];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
-        const int m = m0 + wm * WM + 16 * (2 * ip + ii) + mrow;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           uint32_t amax = 0;
@@ -613,15 +619,40 @@ __device__ __forceinline__ void dgrad2_epilogue_mx8(const LayerArgs& a, const Mx
 #pragma unroll
             for (int v = 0; v < 4; ++v) amax = max(amax, abs_bits(d[h][ii][jj][v]));
           const int X = mx_scale_exp(__uint_as_float(umax_rows4(amax)));
-          const bool ok = m < mlim && c0 < I;
-          const uint32_t row = (uint32_t)m * 2 * I + h * I + c0;
+          xs[2 * ii + h] = X;
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
-            __builtin_amdgcn_raw_buffer_store_b32(
-                mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X), r_qdg,
-                ok ? row + 16 * jj + ncol : OOB, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), r_sdg, (ok && ncol == 0) ? row / 32 : OOB, 0, 0);
+            pk[2 * ii + h][jj] = mx_pack4(d[h][ii][jj][0], d[h][ii][jj][1], d[h][ii][jj][2], d[h][ii][jj][3], X);
         }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        // groups 2,3 of blocks 0,1 <-> groups 0,1 of blocks 2,3
+        auto s = __builtin_amdgcn_permlane32_swap(pk[0][jj], pk[2][jj], false, false);
+        pk[0][jj] = s[0];
+        pk[2][jj] = s[1];
+        s = __builtin_amdgcn_permlane32_swap(pk[1][jj], pk[3][jj], false, false);
+        pk[1][jj] = s[0];
+        pk[3][jj] = s[1];
+        // groups 1,3 of blocks 0,2 <-> groups 0,2 of blocks 1,3
+        s = __builtin_amdgcn_permlane16_swap(pk[0][jj], pk[1][jj], false, false);
+        pk[0][jj] = s[0];
+        pk[1][jj] = s[1];
+        s = __builtin_amdgcn_permlane16_swap(pk[2][jj], pk[3][jj], false, false);
+        pk[2][jj] = s[0];
+        pk[3][jj] = s[1];
+      }
+      {   // now pk[r][jj] of group g = dword r (+4 jj) of block g
+        const int g = lane >> 4;
+        const int m = m0 + wm * WM + 16 * (2 * ip + (g >> 1)) + mrow;
+        const bool ok = m < mlim && c0 < I;
+        const uint32_t row = (uint32_t)m * 2 * I + (g & 1) * I + c0;
+        const int X = g == 0 ? xs[0] : g == 1 ? xs[1] : g == 2 ? xs[2] : xs[3];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pk[0][jj], pk[1][jj], pk[2][jj], pk[3][jj]}, r_qdg,
+                                                 ok ? row + 16 * jj : OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), r_sdg, ok ? row / 32 : OOB, 0, 0);
       }
       // token blocks (32 rows = fragments 2ip, 2ip+1; 16 lanes per column), staged in LDS.
       // The 24 maxima of this sub-block advance through the DPP steps together.

@@ -69,6 +69,7 @@ struct LayerArgs {
   const int32_t* wg_order;        // [E]   expert of each rank (decreasing row count)
   const int32_t* wg_cstart;       // [E+1] first chunk of each rank; wg_cstart[E] = chunks
   const int32_t* wg_slot0;        // [E]   first partial slot of each rank
+  const int32_t* wg_xq;           // [8 * cap] the chunks of each XCD's queue (WgradList::xq)
   float* wpart13;                 // [slots, 2I, H] fp32 partial dW13 of chunks c > 0
   float* wpart2;                  // [slots, H, I]  fp32 partial dW2
   // inputs
@@ -182,15 +183,22 @@ hipError_t route_scratch_ptr(void** ptr);
 #define MOE_WG_KC 4096
 #endif
 constexpr int WG_KC = MOE_WG_KC;
+// Fixed cost of a weight-gradient tile in rows of K (its fp32 output write
+// and pipeline fill), used when the chunks are dealt to the XCD queues.
+constexpr int WG_BETA = 384;
 struct WgradList {              // device tables written by the backward's tile-table kernel
   int32_t* order;               // [E]   expert of each rank, by decreasing row count (ties: index)
   int32_t* cstart;              // [E+1] first chunk of each rank (exclusive prefix of the chunk counts)
   int32_t* slot0;               // [E]   first partial slot of each rank (prefix of chunks - 1)
+  int32_t* xq;                  // [8 * cap] chunks of XCD x's queue at xq[x * cap + q], cap = ceil(chunks / 8),
+                                //           -1 past the queue's end
 };
 // partial slots the split experts can need: sum over experts of (chunks - 1) <= M / WG_KC
 inline size_t wgrad_max_slots(size_t M) { return M / WG_KC; }
 // upper bound of the number of chunks: E + M / WG_KC
 inline int wgrad_max_chunks(int M, int E) { return E + M / WG_KC; }
+// entries of the XCD queue table for max_chunks chunks
+inline int wgrad_queue_slots(int max_chunks) { return 8 * ((max_chunks + 7) / 8); }
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm, int max_tiles,
                              int32_t* tile_expert, int32_t* tile_row0, int32_t* expert_tile0, WgradList wg, hipStream_t s);
@@ -250,20 +258,21 @@ constexpr int FP32_BN = 64;
 inline bool mx8_forward(int mode) { return mode == 2; }
 inline bool mx8_backward(int mode) { return mode == 2 || mode == 3; }
 // Weight-gradient tile of virtual block vb (the block index of a grid with
-// one block per tile): block b goes to XCD b % 8 (round-robin dispatch); in round q the XCDs take chunks 8q .. 8q + 7 of the work list
-// (experts by decreasing row count, an expert's chunks consecutive), XCD x
-// chunk 8q + x in even rounds and 8q + 7 - x in odd ones (a snake, so that no
-// XCD always draws the longest chunk of a round), each as per_e consecutive
-// tiles (which share the chunk's rows in that XCD's L2): the longest tiles
-// start first and the load of the XCDs stays even.
+// one block per tile): block b goes to XCD x = b % 8 (round-robin dispatch),
+// and XCD x takes the chunks of its queue (the tile-table kernel deals the
+// chunks, in work-list order, to the least loaded queue with room; every queue
+// holds at most cap = ceil(chunks / 8)) in order, each as per_e consecutive
+// tiles, which share the chunk's rows in that XCD's L2.
 // Gives the expert e, its rows [r0, r1) (expert-local), the partial slot (-1
-// for chunk 0, which writes dW[e]) and the tile t; false past the last chunk.
+// for chunk 0, which writes dW[e]) and the tile t; false past the queue's end.
 __device__ __forceinline__ bool decode_wgrad_tile(const LayerArgs& a, int vb, int per_e, int& e, int& r0, int& r1,
                                                   int& slot, int& t) {
   const int x = vb % 8, j = vb / 8;
   const int q = j / per_e;
-  const int item = 8 * q + ((q & 1) ? 7 - x : x);
-  if (item >= a.wg_cstart[a.E]) return false;
+  const int cap = (a.wg_cstart[a.E] + 7) / 8;
+  if (q >= cap) return false;
+  const int item = a.wg_xq[x * cap + q];
+  if (item < 0) return false;
   int lo = 0, hi = a.E - 1;               // rank with cstart[rank] <= item (cstart strictly increasing)
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;

@@ -285,7 +285,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
 // experts by decreasing row count, ties by index (longest-processing-time-
 // first list scheduling), each split into chunks of at most WG_KC rows (an
 // empty expert is one empty chunk); chunk c > 0 of an expert accumulates into
-// a partial slot that the ordered reduction adds to chunk 0's result.
+// a partial slot that the ordered reduction adds to chunk 0's result.  The
+// chunks are then dealt to the 8 XCD queues (balanced load).
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                           int max_tiles, int32_t* __restrict__ tile_expert,
                                                           int32_t* __restrict__ tile_row0,
@@ -312,12 +313,14 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   }
   if (wg.order) {
     __shared__ int s_nch[MAX_E];            // chunks of the expert of each rank
+    __shared__ int s_rows[MAX_E];           // rows of the expert of each rank
     if (e < E) {   // rank of e by (count desc, index asc); s_cnt is visible after the scan's barriers
       const int c = s_cnt[e];
       int rank = 0;
       for (int f = 0; f < E; ++f) rank += (s_cnt[f] > c) || (s_cnt[f] == c && f < e);
       wg.order[rank] = e;
       s_nch[rank] = c > WG_KC ? (c + WG_KC - 1) / WG_KC : 1;
+      s_rows[rank] = c;
     }
     __syncthreads();
     // exclusive prefix of the chunk counts over the ranks (Hillis-Steele over
@@ -341,6 +344,54 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
       wg.cstart[e] = excl;
       wg.slot0[e] = excl - e;
       if (e == E - 1) wg.cstart[E] = s_cs[cc][e];
+    }
+    // XCD queues (cap = ceil(chunks / 8) entries each, so that the grid of
+    // the weight-gradient kernels, cap chunk rounds per XCD, covers them all).
+    // Even routing (no expert above twice the mean): the snake deal, filled by
+    // all threads at once -- in round q the XCDs take chunks 8q .. 8q + 7, XCD
+    // x chunk 8q + x in even rounds and 8q + 7 - x in odd ones.  Skewed
+    // routing: the chunks in list order (decreasing rows, so longest
+    // processing time first), each to the queue of least load (rows + WG_BETA
+    // per chunk; ties: lowest XCD) among those holding fewer than cap.  Lanes
+    // 0-7 of the first wave own one queue each; the choice is the minimum over
+    // those lanes of the key load * 8 + lane (3 DPP steps: quad swaps, then
+    // the half-row mirror), so all of them pick the same queue.  The experts'
+    // chunk and row counts arrive 64 at a time (one LDS read per lane, then
+    // readlane).
+    const int n = s_cs[cc][E - 1];
+    const int cap = (n + 7) / 8;
+    const bool skewed = (long long)s_rows[0] * E > 2LL * offsets[E];
+    if (!skewed) {
+      for (int i = e; i < 8 * cap; i += blockDim.x) {
+        const int x = i / cap, q = i % cap;
+        const int item = 8 * q + ((q & 1) ? 7 - x : x);
+        wg.xq[i] = item < n ? item : -1;
+      }
+    } else if (e < 64) {
+      int len = 0, load = 0;
+      int item = 0;
+      for (int r0 = 0; r0 < E; r0 += 64) {
+        const int vn = r0 + e < E ? s_nch[r0 + e] : 0;
+        const int vr = r0 + e < E ? s_rows[r0 + e] : 0;
+        const int nr = min(64, E - r0);
+        for (int l = 0; l < nr; ++l) {
+          const int nch = __builtin_amdgcn_readlane(vn, l), rows_r = __builtin_amdgcn_readlane(vr, l);
+          for (int ch = 0; ch < nch; ++ch, ++item) {
+            const int rows = min(rows_r - ch * WG_KC, WG_KC);
+            uint32_t key = (e < 8 && len < cap) ? (uint32_t)min(load, (1 << 28) - 1) * 8u + (uint32_t)e : UINT_MAX;
+            key = min(key, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)key, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+            key = min(key, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)key, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+            key = min(key, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)key, 0x141, 0xF, 0xF, false));   // row_half_mirror
+            if (e == (int)(key & 7u)) {
+              wg.xq[e * cap + len] = item;
+              ++len;
+              load += rows + WG_BETA;
+            }
+          }
+        }
+      }
+      if (e < 8)
+        for (int q = len; q < cap; ++q) wg.xq[e * cap + q] = -1;
     }
   }
   // s_start[cur][e] = inclusive sum; exclusive start of e = inclusive(e-1)
