@@ -13,6 +13,7 @@ constexpr uint32_t OOB = 0x80000000u;   // buffer offset that reads as zeros
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
+
 // Raw buffer resource over [base, base + bytes): loads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -375,8 +376,11 @@ __device__ __forceinline__ void gemm_epilogue(const LayerArgs& a, f32x4_t (&acc)
         const int m = m0 + ch * CH + c / TPR, n = n0 + 8 * (c % TPR);
         const uint32_t o1 = (m < mlim && n < I) ? (uint32_t)(((size_t)m * 2 * I + n) * 2) : OOB;
         gt[it] = a.gate[ms[it]];
-        r1[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1, 0, 0);
-        r3[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1 == OOB ? OOB : o1 + I * 2, 0, 0);
+        // non-temporal (cache policy 2 = nt): each G13 element is read once
+        // (1.5 % faster; the MXFP8 epilogue's fp32 G13 loads measured 3 %
+        // slower that way and stay plain)
+        r1[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1, 0, 2);
+        r3[it] = __builtin_amdgcn_raw_buffer_load_b128(r_g13, o1 == OOB ? OOB : o1 + I * 2, 0, 2);
       }
       if (ch > 0) __syncthreads();                         // the previous chunk has been read
 #pragma unroll

@@ -29,18 +29,30 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 r, float* out) {
   }
 }
 
+// 16-byte source load; NT = non-temporal, for sources read once (the
+// weights: W13 0.30 -> 0.28 ms, W2 0.15 -> 0.13 for both layouts).  The
+// gathered token rows, read once per routed slot, stay cached (non-temporal
+// there: 0.13 -> 0.17 ms).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+template <bool NT = false>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  u32x4v w;
+  if constexpr (NT) w = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  else w = *reinterpret_cast<const u32x4v*>(p);
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // 32 consecutive elements of a row, bf16 or fp32
 __device__ __forceinline__ void load32(const bf16_t* p, float (&v)[32]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) unpack_bf16x8(q[i], v + 8 * i);
+  for (int i = 0; i < 4; ++i) unpack_bf16x8(ld16(p + 8 * i), v + 8 * i);
 }
 __device__ __forceinline__ void load32(const float* p, float (&v)[32]) {
-  const f32x4_t* q = reinterpret_cast<const f32x4_t*>(p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const f32x4_t w = q[i];
-    v[4 * i] = w[0]; v[4 * i + 1] = w[1]; v[4 * i + 2] = w[2]; v[4 * i + 3] = w[3];
+    const uint4 w = ld16(p + 4 * i);
+    v[4 * i] = __uint_as_float(w.x); v[4 * i + 1] = __uint_as_float(w.y);
+    v[4 * i + 2] = __uint_as_float(w.z); v[4 * i + 3] = __uint_as_float(w.w);
   }
 }
 
@@ -167,8 +179,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const T* __restrict__ s
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int sr = s_src[r0 + p * RPP];
-      raw[p] = (sr >= 0 && fc < F) ? *reinterpret_cast<const uint4*>(src + (size_t)sr * F + fc)
-                                   : make_uint4(0u, 0u, 0u, 0u);
+      raw[p] = (sr >= 0 && fc < F) ? ld16<!GROUPED>(src + (size_t)sr * F + fc) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) *reinterpret_cast<uint4*>(&s_tile[(r0 + p * RPP) * QT_LD + c * EPC]) = raw[p];
