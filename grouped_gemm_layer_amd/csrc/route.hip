@@ -102,6 +102,89 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   }
 }
 
+// k <= 8: four lanes per token, 64 tokens per block.  Lane q of a token scans
+// experts [q E/4, (q+1) E/4) in ascending order and keeps the 8 best (value,
+// expert) pairs sorted in registers: a new value enters before the first slot
+// it beats strictly, so an equal value with a larger id stays behind (the key
+// (-logit, id)).  Then the lists of lanes q and q^1, and of q and q^2, merge
+// through DPP quad swaps, the higher lane's pairs (all with larger ids)
+// inserted into the lower lane's list by the same rule; lane 0 of the quad
+// ends with the token's top k, in order, and its softmax gates.
+constexpr int TOPK_SMALL = 8;
+__device__ __forceinline__ void topk_insert(float x, int id, float (&v)[TOPK_SMALL], int (&ix)[TOPK_SMALL]) {
+  // slot j becomes: itself if x does not beat it, x if x beats it but not
+  // slot j - 1, else the old slot j - 1 (shifted down); from the last slot up
+#pragma unroll
+  for (int j = TOPK_SMALL - 1; j >= 0; --j) {
+    const bool c = x > v[j];
+    const bool cp = j > 0 && x > v[j > 0 ? j - 1 : 0];
+    const float nv = cp ? v[j > 0 ? j - 1 : 0] : x;
+    const int ni = cp ? ix[j > 0 ? j - 1 : 0] : id;
+    v[j] = c ? nv : v[j];
+    ix[j] = c ? ni : ix[j];
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void topk_merge(float (&v)[TOPK_SMALL], int (&ix)[TOPK_SMALL], bool lower) {
+  float pv[TOPK_SMALL];
+  int pi[TOPK_SMALL];
+#pragma unroll
+  for (int j = 0; j < TOPK_SMALL; ++j) {
+    pv[j] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[j]), CTRL, 0xF, 0xF, false));
+    pi[j] = __builtin_amdgcn_update_dpp(0, ix[j], CTRL, 0xF, 0xF, false);
+  }
+  if (lower) {
+#pragma unroll
+    for (int j = 0; j < TOPK_SMALL; ++j) topk_insert(pv[j], pi[j], v, ix);
+  }
+}
+__global__ __launch_bounds__(256) void topk_gate_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int k, int32_t* __restrict__ idx,
+                                                              float* __restrict__ gate) {
+  const int q = threadIdx.x & 3;
+  const int t = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const bool live = t < T;     // no early exit: the merges read the whole quad
+  float v[TOPK_SMALL];
+  int ix[TOPK_SMALL];
+#pragma unroll
+  for (int j = 0; j < TOPK_SMALL; ++j) {
+    v[j] = -INFINITY;
+    ix[j] = INT_MAX;
+  }
+  const int per = (E + 3) / 4;
+  const int e0 = min(E, q * per), e1 = min(E, e0 + per);
+  if (live) {
+    const float* row = logits + (size_t)t * E;
+    if ((E & 3) == 0 && (per & 3) == 0) {   // 16-byte aligned quarters
+      for (int e = e0; e < e1; e += 4) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(row + e);
+        topk_insert(x[0], e, v, ix);
+        topk_insert(x[1], e + 1, v, ix);
+        topk_insert(x[2], e + 2, v, ix);
+        topk_insert(x[3], e + 3, v, ix);
+      }
+    } else {
+      for (int e = e0; e < e1; ++e) topk_insert(row[e], e, v, ix);
+    }
+  }
+  topk_merge<0xB1>(v, ix, (q & 1) == 0);   // quad_perm 1,0,3,2: lanes q, q^1
+  topk_merge<0x4E>(v, ix, (q & 2) == 0);   // quad_perm 2,3,0,1: lanes q, q^2
+  if (live && q == 0) {
+    float ex[TOPK_SMALL], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < TOPK_SMALL; ++j) {
+      ex[j] = j < k ? expf(v[j] - v[0]) : 0.f;
+      sum += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < TOPK_SMALL; ++j)
+      if (j < k) {
+        idx[(size_t)t * k + j] = ix[j];
+        gate[(size_t)t * k + j] = ex[j] / sum;
+      }
+  }
+}
+
 // Per-block expert histogram of ROUTE_CHUNK flat slots.
 __global__ __launch_bounds__(256) void expert_hist_kernel(const int32_t* __restrict__ idx, int M, int E,
                                                           int32_t* __restrict__ partials) {
@@ -266,7 +349,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
   const int nblk = route_num_blocks(M);
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
-  hipError_t e = launch_kernel(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, gate);
+  hipError_t e = k <= TOPK_SMALL
+                    ? launch_kernel(topk_gate_small_kernel, dim3((T + 63) / 64), dim3(256), 0, s, logits, T, E, k,
+                                    topk_idx, gate)
+                    : launch_kernel(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx,
+                                    gate);
   if (e == hipSuccess)
     e = launch_kernel(expert_hist_kernel, dim3(nblk), dim3(256), 0, s, (const int32_t*)topk_idx, M, E, ws_partials);
   if (e == hipSuccess)

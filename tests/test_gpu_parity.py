@@ -197,11 +197,13 @@ def test_determinism_bitwise():
     (3000, 512, 32, True, 121),    # the same with many ties at the top-k boundary
     (5000, 96, 5, False, 122),     # lanes 32..63 hold one logit
     (700, 8, 8, True, 123),        # k = E < 64: most lanes hold none
+    (2000, 130, 8, True, 124),     # k <= 8 path: quarters of 33 experts, the last one 31, scalar loads
 ])
 def test_route_extremes_exact(T, E, k, ties, seed):
     """Routing at the ends of the supported range (E up to 512, k up to 32)
     matches the oracle bit for bit: the wave arg-max over (value, expert)
-    pairs and the batched expert scan."""
+    pairs (k > 8), the four-lanes-per-token selection (k <= 8) and the batched
+    expert scan."""
     d = mi.LayerDims(T=T, H=64, I=64, E=E, k=k, dtype="bf16")
     print(f"[parity] route T={T} E={E} k={k} ties={ties}", flush=True)
     inp = mi.make_inputs(d, seed)
