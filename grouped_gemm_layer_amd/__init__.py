@@ -126,12 +126,19 @@ def load_library():
     lib.moe_mxfp8_grouped_capacity.restype = sz
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_wgrad_chunk_rows.argtypes = []
+    lib.moe_wgrad_chunk_rows.restype = ctypes.c_int32
     _lib = lib
     return lib
 
 
 def status_str(status: int) -> str:
     return load_library().moe_status_str(status).decode()
+
+
+def wgrad_chunk_rows() -> int:
+    """Rows per weight-gradient chunk (experts with more rows are split)."""
+    return int(load_library().moe_wgrad_chunk_rows())
 
 
 def _check(st: int, what: str):

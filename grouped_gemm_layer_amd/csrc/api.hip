@@ -679,6 +679,8 @@ size_t moe_mxfp8_grouped_capacity(int32_t rows, int32_t E) {
   return mx_token_capacity((size_t)rows, E);
 }
 
+int32_t moe_wgrad_chunk_rows(void) { return WG_KC; }
+
 const char* moe_status_str(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -201,8 +201,9 @@ moe_status moe_forward_recompute(const moe_dims* dims, const void* x, const void
  *   dx[t] = sum_j (dG13 W13[e])[row of slot j]       (fp32 sum in slot order)
  *   dw2[e]  = sum_r dy[t(r)]^T (gate_r A_r)          (fp32 accumulate and output)
  *   dw13[e] = sum_r dG13_r^T x[t(r)]                 (fp32; zero for an empty expert)
- *     (an expert with more than 4096 rows sums these over chunks of 4096 rows,
- *     each accumulated in fp32, then added in chunk order: deterministic)
+ *     (an expert with more than moe_wgrad_chunk_rows() rows, 8192, sums these
+ *     over chunks of that many rows, each accumulated in fp32, then added in
+ *     chunk order: deterministic)
  *   dlogits[t,e] = gate_e (dgate_e - sum_j gate_j dgate_j) on the top-k set, else 0
  * dy, x, w13, w2: device inputs; saved: from moe_forward; dx: device [T,H];
  * dw13, dw2: device fp32, overwritten; dgate: device [T,k] fp32; dlogits:
@@ -340,6 +341,13 @@ moe_status moe_mxfp8_quantize_grouped(const void* src, int32_t rows, int32_t col
                                       int32_t E, int32_t capacity, int32_t* pad_off, uint8_t* codes,
                                       uint8_t* scales, hipStream_t stream);
 size_t moe_mxfp8_grouped_capacity(int32_t rows, int32_t E);
+
+/* Rows per weight-gradient chunk.  An expert with more routed rows has its
+ * weight gradients computed in chunks of this many rows (split along K) whose
+ * fp32 partial sums are added in chunk order (so such an expert's dW differs
+ * from a single-pass sum by fp32 rounding only).  A constant of the library
+ * build; no GPU needed. */
+int32_t moe_wgrad_chunk_rows(void);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status status);

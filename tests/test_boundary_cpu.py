@@ -323,3 +323,10 @@ def test_weight_codes_sizes_and_errors():
               16, None) == 5
     assert bc(ctypes.byref(g.Dims.of(T, H, I, E, k, "bf16")), t(0), t(1), t(3), ctypes.byref(c), t(4), t(5), t(6),
               t(7), t(8), None, t(9), 1 << 30, None) == 3
+
+def test_wgrad_chunk_rows():
+    """The weight-gradient chunk size is a positive multiple of the 128-row
+    MXFP8 K tile (chunk boundaries must fall on K tiles)."""
+    import grouped_gemm_layer_amd as g
+    kc = g.wgrad_chunk_rows()
+    assert kc > 0 and kc % 128 == 0

@@ -37,6 +37,7 @@ which shows as up to a few 1e-2 of max|ref| in dX and dW13, and nowhere else.
 import numpy as np
 import pytest
 
+import grouped_gemm_layer_amd as gl
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 from _layer_harness import GpuRun, relerr, to_dev, to_np, check_routing_exact, record_errors
@@ -188,15 +189,17 @@ def test_fp8_bwd_one_expert_takes_all():
 
 
 def test_fp8_bwd_split_heavy_expert():
-    """MXFP8 weight gradients of experts split into several 4096-row chunks
-    (chunk boundaries fall on 128-row K tiles of the padded token operands)."""
-    d = mi.LayerDims(T=9000, H=256, I=64, E=4, k=2, dtype="bf16", mode="fp8_bwd")
+    """MXFP8 weight gradients of experts split into several chunks of
+    moe_wgrad_chunk_rows rows (chunk boundaries fall on 128-row K tiles of the
+    padded token operands): expert 0 in three chunks, expert 1 in two."""
+    kc = gl.wgrad_chunk_rows()
+    d = mi.LayerDims(T=17000, H=256, I=64, E=4, k=2, dtype="bf16", mode="fp8_bwd")
     inp = mi.make_inputs(d, 306)
     inp["logits"][:, 0] += 4.0            # moderate biases: no gate underflows
     inp["logits"][: d.T // 2, 1] += 2.0
     run = _compare_fp8_bwd(d, inp)
     c = run.routing_np()["counts"]
-    assert c[0] > 2 * 4096 and c[1] > 4096
+    assert c[0] > 2 * kc and c[1] > kc
 
 
 def _oracle_workers():
@@ -284,7 +287,7 @@ def test_fp8_bwd_fullsize_skewed_whole():
     import dataclasses
     d = dataclasses.replace(mi.CONFIGS[3], mode="fp8_bwd")
     r = _fullsize_compare(d, 3, "fp8_bwd/config3_skew", TOL_QORACLE, False)
-    assert (r.counts == 0).sum() >= 1 and r.counts.max() > 4096
+    assert (r.counts == 0).sum() >= 1 and r.counts.max() > gl.wgrad_chunk_rows()
 
 
 # ---------------------------------------------------------------------------

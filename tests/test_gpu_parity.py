@@ -8,6 +8,7 @@ for bf16 (the layer's stated tolerance) and <= 1e-4 for fp32.
 import numpy as np
 import pytest
 
+import grouped_gemm_layer_amd as gl
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 from _layer_harness import GpuRun, relerr, to_np, check_routing_exact, record_errors
@@ -80,24 +81,26 @@ def test_edge_all_tokens_to_one_expert():
 
 
 def test_wgrad_split_heavy_expert():
-    """Experts with more rows than one weight-gradient chunk (4096 rows): their
-    dW13 and dW2 are summed from several chunks in chunk order.  Expert 0
-    takes every token (9000 rows: three chunks), expert 1 at least half of
-    them (two chunks), the rest a few hundred each."""
-    d = mi.LayerDims(T=9000, H=128, I=64, E=4, k=2, dtype="bf16")
+    """Experts with more rows than one weight-gradient chunk
+    (moe_wgrad_chunk_rows, 8192): their dW13 and dW2 are summed from several
+    chunks in chunk order.  Expert 0 takes every token (17000 rows: three
+    chunks), expert 1 at least half of them (two chunks), the rest a few
+    hundred each."""
+    kc = gl.wgrad_chunk_rows()
+    d = mi.LayerDims(T=17000, H=128, I=64, E=4, k=2, dtype="bf16")
     inp = mi.make_inputs(d, 111)
     inp["logits"][:, 0] += 4.0            # moderate biases: no gate underflows
     inp["logits"][: d.T // 2, 1] += 2.0
     run, _ = _full_compare(d, inp, TOL["bf16"])
     c = run.routing_np()["counts"]
-    assert c[0] > 2 * 4096 and c[1] > 4096
+    assert c[0] > 2 * kc and c[1] > kc
 
 
 @pytest.mark.parametrize("dims,seed", [
     (mi.LayerDims(T=300, H=128, I=64, E=8, k=2, dtype="fp32"), 112),
     (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True), 113),
     (mi.LayerDims(T=600, H=256, I=128, E=8, k=4, dtype="bf16", skew=True, mode="fp8_bwd"), 114),
-    (mi.LayerDims(T=9000, H=128, I=64, E=4, k=2, dtype="bf16"), 115),   # split experts
+    (mi.LayerDims(T=17000, H=128, I=64, E=4, k=2, dtype="bf16"), 115),   # split experts
 ])
 def test_backward_accumulate_into(dims, seed):
     """moe_backward_accumulate adds the weight gradients to what dw13 / dw2
@@ -111,7 +114,7 @@ def test_backward_accumulate_into(dims, seed):
     bar, whichever is larger)."""
     import torch
     inp = mi.make_inputs(dims, seed)
-    if dims.T == 9000:
+    if dims.T == 17000:
         inp["logits"][:, 0] += 4.0
         inp["logits"][: dims.T // 2, 1] += 2.0
     print(f"[accumulate] dims={dims}", flush=True)
@@ -130,9 +133,10 @@ def test_backward_accumulate_into(dims, seed):
     for a, b in zip((L.dx, L.dgate, L.dlogits), others):
         assert torch.equal(a, b)
     counts = run.routing_np()["counts"]
+    kc = gl.wgrad_chunk_rows()
     for got, R, G in ((L.dw13, R13, G13), (L.dw2, R2, G2)):
         for e in range(dims.E):
-            if counts[e] <= 4096:
+            if counts[e] <= kc:
                 assert torch.equal(got[e], R[e] + G[e]), e
             else:
                 err = (got[e] - (R[e] + G[e])).abs().max().item()
