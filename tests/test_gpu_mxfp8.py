@@ -281,6 +281,16 @@ def test_fp8_bwd_fullsize_whole():
 
 
 @pytest.mark.timeout(900)
+def test_fp8_bwd_235b_whole():
+    """fp8_bwd at the Qwen3-235B-A22B expert shape (H 4096, I 1536): every
+    element against both oracles, as at the 30B shape (four times the operand
+    and code buffers, the largest MXFP8 offsets the workloads reach)."""
+    import dataclasses
+    d = dataclasses.replace(mi.CONFIGS[4], mode="fp8_bwd")
+    _fullsize_compare(d, 4, "fp8_bwd/config4", TOL_QORACLE, False)
+
+
+@pytest.mark.timeout(900)
 def test_fp8_bwd_fullsize_skewed_whole():
     """The same with the Zipf-skewed routing: hot experts split into several
     weight-gradient chunks, empty experts with zero weight gradients."""
