@@ -365,3 +365,11 @@ def test_mxfp8_mode_fullsize_whole():
     the benchmark times; every element against both oracles."""
     import dataclasses
     _fullsize_compare(dataclasses.replace(mi.CONFIGS[2], mode="mxfp8"), 2, "mxfp8/config2", TOL_Q_MXFP8, True)
+
+
+@pytest.mark.timeout(900)
+def test_mxfp8_mode_235b_whole():
+    """mxfp8 mode at the Qwen3-235B-A22B expert shape: every element against
+    both oracles."""
+    import dataclasses
+    _fullsize_compare(dataclasses.replace(mi.CONFIGS[4], mode="mxfp8"), 4, "mxfp8/config4", TOL_Q_MXFP8, True)
