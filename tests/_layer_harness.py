@@ -32,6 +32,27 @@ def record_errors(test: str, errs: dict, bars: dict) -> None:
             f.write(json.dumps(rec) + "\n")
 
 
+# The exact fp64 layer (oracle forward and backward) of full-size inputs,
+# computed once per test process: the bf16, fp8_bwd and mxfp8 full-size tests
+# of one shape draw the same inputs (seed = configuration number, the mode does
+# not change them), and at the 235B shape the oracle takes about a minute.
+_EXACT = {}
+
+
+def exact_layer(d, seed: int, inp: dict, r):
+    """(outputs, forward state) of the oracle for the inputs drawn by
+    make_inputs(d, seed): outputs y, dx, dgate, dlogits, dw2, dw13, and the
+    state the oracle's forward hands its backward; callers only read them."""
+    from oracle import moe_oracle as orc
+    key = (d.T, d.H, d.I, d.E, d.k, d.dtype, d.skew, seed)
+    if key not in _EXACT:
+        y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
+        ref = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
+        ref["y"] = y
+        _EXACT[key] = (ref, st)
+    return _EXACT[key]
+
+
 def to_dev(a: np.ndarray, dtype):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a))

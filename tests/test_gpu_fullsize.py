@@ -13,7 +13,7 @@ import pytest
 
 import moe_inputs as mi
 from oracle import moe_oracle as orc
-from _layer_harness import GpuRun, relerr, to_np, check_routing_exact, record_errors
+from _layer_harness import GpuRun, relerr, to_np, check_routing_exact, record_errors, exact_layer
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -54,13 +54,10 @@ def test_fullsize_whole(cfg):
         assert torch.count_nonzero(L.dw13[int(e)]).item() == 0 and torch.count_nonzero(L.dw2[int(e)]).item() == 0
 
     # the whole layer through the oracle
-    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
-    errs = {"y": relerr(to_np(L.y), Y)}
-    del Y
-    ref = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
-    del st
+    ref, _ = exact_layer(d, cfg, inp, r)
+    errs = {"y": relerr(to_np(L.y), ref["y"])}
     for key, t in (("dx", L.dx), ("dgate", L.dgate), ("dlogits", L.dlogits), ("dw2", L.dw2), ("dw13", L.dw13)):
-        errs[key] = relerr(to_np(t), ref.pop(key))
+        errs[key] = relerr(to_np(t), ref[key])
     record_errors(f"fullsize/config{cfg}", errs, {k: TOL for k in errs})
     for k, v in errs.items():
         assert v <= TOL, (k, v)

@@ -40,7 +40,7 @@ import pytest
 import grouped_gemm_layer_amd as gl
 import moe_inputs as mi
 from oracle import moe_oracle as orc
-from _layer_harness import GpuRun, relerr, to_dev, to_np, check_routing_exact, record_errors
+from _layer_harness import GpuRun, relerr, to_dev, to_np, check_routing_exact, record_errors, exact_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -228,16 +228,13 @@ def _fullsize_compare(d, seed, tag, tol_q, fwd_mx8):
         assert np.all(got["dw13"][e] == 0) and np.all(got["dw2"][e] == 0)
     del run, L
     w = _oracle_workers()
-    Y, st = orc.forward(inp["x"], inp["w13"], inp["w2"], r)
-    exact = orc.backward(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, st)
-    exact["y"] = Y
+    exact, st = exact_layer(d, seed, inp, r)
     if fwd_mx8:
         Yq, stq = orc.forward_mxfp8(inp["x"], inp["w13"], inp["w2"], r, workers=w)
     else:
-        Yq, stq = Y, st
+        Yq, stq = exact["y"], st
     quant = orc.backward_mxfp8(inp["dy"], inp["x"], inp["w13"], inp["w2"], r, stq, workers=w)
     quant["y"] = Yq
-    del st
     e_q = {k: relerr(got[k], quant[k]) for k in got}
     e_x = {k: relerr(got[k], exact[k]) for k in got}
     e_qx = {k: relerr(quant[k], exact[k]) for k in got}
