@@ -185,19 +185,20 @@ __global__ __launch_bounds__(256) void topk_gate_small_kernel(const float* __res
   }
 }
 
-// Per-block expert histogram of ROUTE_CHUNK flat slots.
-__global__ __launch_bounds__(256) void expert_hist_kernel(const int32_t* __restrict__ idx, int M, int E,
-                                                          int32_t* __restrict__ partials) {
+// Per-block expert histogram of ROUTE_CHUNK flat slots (1024 threads).
+constexpr int ROUTE_THREADS = 1024;   // threads of the histogram and scatter blocks
+__global__ __launch_bounds__(ROUTE_THREADS) void expert_hist_kernel(const int32_t* __restrict__ idx, int M, int E,
+                                                                    int32_t* __restrict__ partials) {
   __shared__ int s_hist[MAX_E];
-  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) s_hist[e] = 0;
   __syncthreads();
   const int base = blockIdx.x * ROUTE_CHUNK;
-  for (int i = threadIdx.x; i < ROUTE_CHUNK; i += 256) {
+  for (int i = threadIdx.x; i < ROUTE_CHUNK; i += ROUTE_THREADS) {
     const int f = base + i;
     if (f < M) atomicAdd(&s_hist[idx[f]], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) partials[blockIdx.x * E + e] = s_hist[e];
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) partials[blockIdx.x * E + e] = s_hist[e];
 }
 
 // One block: counts, offsets and the expert-major block bases
@@ -256,24 +257,29 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
 }
 
 // Stable scatter: slot f of expert e goes to bases[b][e] + (number of earlier
-// slots of the same block routed to e).  Earlier = smaller flat index.
-__global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* __restrict__ idx, int M, int E,
-                                                             int ebits, const int32_t* __restrict__ bases,
-                                                             int32_t* __restrict__ s2f,
-                                                             int32_t* __restrict__ f2s) {
+// slots of the same block routed to e).  Earlier = smaller flat index.  Each
+// round takes ROUTE_THREADS consecutive slots: a slot's rank among the slots
+// of its wave routed to the same expert comes from ballots over the expert's
+// bits, the waves before it add their counts (LDS, in wave order).
+constexpr int ROUTE_WAVES = ROUTE_THREADS / 64;
+__global__ __launch_bounds__(ROUTE_THREADS) void expert_scatter_kernel(const int32_t* __restrict__ idx, int M, int E,
+                                                                       int ebits, const int32_t* __restrict__ bases,
+                                                                       int32_t* __restrict__ s2f,
+                                                                       int32_t* __restrict__ f2s) {
   __shared__ int s_run[MAX_E];
-  __shared__ int s_wc[4][MAX_E];
+  __shared__ int s_wc[ROUTE_WAVES][MAX_E];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
     s_run[e] = bases[blockIdx.x * E + e];
-    s_wc[0][e] = s_wc[1][e] = s_wc[2][e] = s_wc[3][e] = 0;
+#pragma unroll
+    for (int w = 0; w < ROUTE_WAVES; ++w) s_wc[w][e] = 0;
   }
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int base = blockIdx.x * ROUTE_CHUNK;
-  for (int round = 0; round < ROUTE_CHUNK / 256; ++round) {
-    const int f = base + round * 256 + threadIdx.x;
+  for (int round = 0; round < ROUTE_CHUNK / ROUTE_THREADS; ++round) {
+    const int f = base + round * ROUTE_THREADS + threadIdx.x;
     const bool valid = f < M;
     const int e = valid ? idx[f] : 0;
     uint64_t same = __ballot(valid);
@@ -292,9 +298,14 @@ __global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* __re
       f2s[f] = pos;
     }
     __syncthreads();
-    for (int ee = threadIdx.x; ee < E; ee += 256) {
-      s_run[ee] += s_wc[0][ee] + s_wc[1][ee] + s_wc[2][ee] + s_wc[3][ee];
-      s_wc[0][ee] = s_wc[1][ee] = s_wc[2][ee] = s_wc[3][ee] = 0;
+    for (int ee = threadIdx.x; ee < E; ee += ROUTE_THREADS) {
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < ROUTE_WAVES; ++w) {
+        sum += s_wc[w][ee];
+        s_wc[w][ee] = 0;
+      }
+      s_run[ee] += sum;
     }
     __syncthreads();
   }
@@ -355,13 +366,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* topk_
                     : launch_kernel(topk_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx,
                                     gate);
   if (e == hipSuccess)
-    e = launch_kernel(expert_hist_kernel, dim3(nblk), dim3(256), 0, s, (const int32_t*)topk_idx, M, E, ws_partials);
+    e = launch_kernel(expert_hist_kernel, dim3(nblk), dim3(ROUTE_THREADS), 0, s, (const int32_t*)topk_idx, M, E,
+                      ws_partials);
   if (e == hipSuccess)
     e = launch_kernel(expert_scan_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)ws_partials, nblk, E, ws_bases,
                       counts, offsets);
   if (e == hipSuccess)
-    e = launch_kernel(expert_scatter_kernel, dim3(nblk), dim3(256), 0, s, (const int32_t*)topk_idx, M, E, ebits,
-                      (const int32_t*)ws_bases, s2f, f2s);
+    e = launch_kernel(expert_scatter_kernel, dim3(nblk), dim3(ROUTE_THREADS), 0, s, (const int32_t*)topk_idx, M, E,
+                      ebits, (const int32_t*)ws_bases, s2f, f2s);
   return e;
 }
 
