@@ -214,20 +214,36 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
   //   KO tile [64 k][R]: k = (1024*ci + 16*l) / (2R); the 32-byte granule at
   //     physical position g holds logical granule g ^ f(k).
   const int w_uni = __builtin_amdgcn_readfirstlane(wave);
+  // KC source offset of this lane's 16 bytes in 1 KiB block ci of the A / B tile
+  auto a_kc_off = [&](int ci) __attribute__((always_inline)) -> uint32_t {
+    const int rl = (512 / BK) * ci + lane / (BK / 8);
+    const int row = min(m0 + rl, mlim - 1);   // rows past the segment: any valid row
+    const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(rl);
+    uint32_t o;
+    if constexpr (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) o = (uint32_t)(a.s2f[row] / k) * H;
+    else if constexpr (KIND == KIND_FWD2) o = (uint32_t)row * I;
+    else o = (uint32_t)row * 2 * I;
+    return (o + chunk * 8) * 2;
+  };
+  auto b_kc_off = [&](int ci) __attribute__((always_inline)) -> uint32_t {
+    const int nl = (512 / BK) * ci + lane / (BK / 8);
+    const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(nl);
+    uint32_t o;
+    if constexpr (KIND == KIND_FWD1) {
+      const int c = min(n0 + (nl & (BN / 2 - 1)), I - 1);
+      o = (uint32_t)((nl < BN / 2) ? c : I + c) * H;
+    } else {
+      o = (uint32_t)min(n0 + nl, H - 1) * I;
+    }
+    return (o + chunk * 8) * 2;
+  };
   uint32_t oa[DA], ob[DB];   // KC: byte offset of row + logical chunk; KO: byte offset of the columns
   int ka[K_::a_ko ? DA : 1], kb[K_::b_ko ? DB : 1];   // KO: k-row of the chunk inside the tile
 #pragma unroll
   for (int i = 0; i < DA; ++i) {
     const int ci = i * NW + w_uni;
     if constexpr (!K_::a_ko) {
-      const int rl = (512 / BK) * ci + lane / (BK / 8);
-      const int row = min(m0 + rl, mlim - 1);   // rows past the segment: any valid row
-      const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(rl);
-      uint32_t o;
-      if constexpr (KIND == KIND_FWD1 || KIND == KIND_DGRAD2) o = (uint32_t)(a.s2f[row] / k) * H;
-      else if constexpr (KIND == KIND_FWD2) o = (uint32_t)row * I;
-      else o = (uint32_t)row * 2 * I;
-      oa[i] = (o + chunk * 8) * 2;
+      oa[i] = a_kc_off(ci);
     } else {
       const int p = 1024 * ci + 16 * lane;
       const int kk = p / (BM * 2), byte = p % (BM * 2);
@@ -240,16 +256,7 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
   for (int i = 0; i < DB; ++i) {
     const int ci = i * NW + w_uni;
     if constexpr (!K_::b_ko) {
-      const int nl = (512 / BK) * ci + lane / (BK / 8);
-      const int chunk = (lane % (BK / 8)) ^ kc_swz<BK>(nl);
-      uint32_t o;
-      if constexpr (KIND == KIND_FWD1) {
-        const int c = min(n0 + (nl & (BN / 2 - 1)), I - 1);
-        o = (uint32_t)((nl < BN / 2) ? c : I + c) * H;
-      } else {
-        o = (uint32_t)min(n0 + nl, H - 1) * I;
-      }
-      ob[i] = (o + chunk * 8) * 2;
+      ob[i] = b_kc_off(ci);
     } else {
       const int p = 1024 * ci + 16 * lane;
       const int kk = p / (BN * 2), byte = p % (BN * 2);
@@ -393,7 +400,142 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
   // computes nothing it would store: it keeps its share of the DMA and the
   // barriers and skips its fragment reads and MFMAs.
   const bool idle = K_::ragged_rows && __builtin_amdgcn_readfirstlane((int)(m0 + wm * WM >= mlim)) != 0;
-  if constexpr (C::PIPE) {
+  if constexpr (C::PIPE == 2) {
+    // Ping-pong between the two wave rows, P (row 0) and Q (row 1); each SIMD
+    // holds one wave of each.  Block barriers split the loop into phases: P
+    // reads its fragments of K tile t in phase 2t and multiplies them in
+    // phase 2t+1, Q reads them in phase 2t+1 and multiplies them in phase
+    // 2t+2, so that in every phase one wave of a SIMD feeds the matrix core
+    // while the other waits on the LDS.  Each group loads the half of the A
+    // tile that only it reads, during its MFMAs; Q also loads the B tile,
+    // ahead of its A half, since P reads it one phase earlier.  A stage is
+    // free once Q has read it (phase 2t+1), so tile t+2 lands in the stage of
+    // tile t: P's half from phase 2t+1, Q's part from phase 2t+2.
+    static_assert(C::WGM == 2 && S == 2 && !K_::a_ko && K_::ragged_rows,
+                  "ping-pong main loop: row kinds with a K-contiguous A, two wave rows, two stages");
+    constexpr int NG = NW / 2;                          // waves per group
+    constexpr int PA = (BM / 2) * BK * 2 / 1024 / NG;   // DMAs per wave and tile: its group's half of A
+    constexpr int PB = BN * BK * 2 / 1024 / NG;         // DMAs per Q wave and tile: the B tile
+    static_assert(PA * NG * 1024 == (BM / 2) * BK * 2 && PB * NG * 1024 == BN * BK * 2, "1 KiB DMA blocks");
+    const bool gq = w_uni / C::WGN == 1;                // wave row 1 (uniform: from the read-first-lane wave index)
+    const int wg = w_uni % NG;
+    const int a_blk0 = (gq ? PA * NG : 0) + wg;         // first A-tile block of this wave
+    uint32_t pa[PA], pb[PB];
+    int pkb[K_::b_ko ? PB : 1];   // KO B: k-row of the block inside the tile
+#pragma unroll
+    for (int i = 0; i < PA; ++i) pa[i] = a_kc_off(a_blk0 + i * NG);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int ci = i * NG + wg;
+      if constexpr (!K_::b_ko) {
+        pb[i] = b_kc_off(ci);
+      } else {   // as the KO B offsets above
+        const int p = 1024 * ci + 16 * lane;
+        const int kk = p / (BN * 2), byte = p % (BN * 2);
+        const int col = ((((byte >> 5) ^ ko_f<BN>(kk))) << 4) + ((byte >> 4) & 1) * 8;
+        pkb[i] = kk;
+        pb[i] = min(n0 + col, nlim - 8) * 2;
+      }
+    }
+    auto dma_a = [&](int kt, int st, int i) __attribute__((always_inline)) {
+      dma16(ra_src, kt < nk ? pa[i] + (uint32_t)kt * (BK * 2) : OOB,
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st * STAGE * 2 + (a_blk0 + i * NG) * 1024)));
+    };
+    auto dma_b = [&](int kt, int st, int i) __attribute__((always_inline)) {
+      uint32_t off;
+      if constexpr (!K_::b_ko) off = pb[i] + (uint32_t)kt * (BK * 2);
+      else off = (uint32_t)(kt * BK + pkb[i]) * (KIND == KIND_DGRAD2 ? I * 2 : H * 2) + pb[i];
+      dma16(rb_src, kt < nk ? off : OOB,
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st * STAGE * 2 + BM * BK * 2 + (i * NG + wg) * 1024)));
+    };
+    // Q's DMAs of a tile: the B tile first, then its A half
+    auto dma_q = [&](int kt, int st, int q) __attribute__((always_inline)) {
+      if (q < PB) dma_b(kt, st, q);
+      else dma_a(kt, st, q - PB);
+    };
+    // a whole K tile's MFMAs with ND DMAs spread between them
+    auto mfmas_spread = [&](const AFrag& af, const BFrag& bfr, auto nd, auto&& issue) __attribute__((always_inline)) {
+      constexpr int NM = (BK / 32) * FM * FN, ND = decltype(nd)::value;
+      constexpr int SP = NM / ND > 0 ? NM / ND : 1;
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int idx = (ks * FM + i) * FN + j;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
+            if (idx % SP == SP - 1 && idx / SP < ND) {
+              issue(idx / SP);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+#pragma unroll
+      for (int q = NM / SP; q < ND; ++q) issue(q);
+    };
+    auto phase_end = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // Both groups run "read tile t, barrier, multiply tile t, barrier" loops
+    // with the same barrier count; Q's loop starts one phase later and P
+    // passes one barrier more at the end.  One loop per group and per idle
+    // state, so that no branch splits the MFMA stream.
+    auto pp_loop = [&](auto q_c, auto idle_c) __attribute__((always_inline)) {
+      constexpr bool GQ = decltype(q_c)::value, IDLE = decltype(idle_c)::value;
+      constexpr int ND = GQ ? PB + PA : PA;   // DMAs per tile of this wave
+      auto dma_tile = [&](int kt, int st, int q) __attribute__((always_inline)) {
+        if constexpr (GQ) dma_q(kt, st, q);
+        else dma_a(kt, st, q);
+      };
+      AFrag af;
+      BFrag bfr;
+#pragma unroll
+      for (int q = 0; q < ND; ++q) dma_tile(0, 0, q);
+#pragma unroll
+      for (int q = 0; q < ND; ++q) dma_tile(1, 1, q);
+      if constexpr (GQ) {
+        vm_wait<2 * PA + PB>();   // the B tile of tile 0, before P reads it (phase 0)
+        phase_end();
+        vm_wait<PB + PA>();       // its A half of tile 0, before it reads it (phase 1)
+      } else {
+        vm_wait<PA>();            // its A half of tile 0
+      }
+      phase_end();
+      for (int t = 0; t < nk; ++t) {
+        const int st = t & 1;
+        // read tile t (P: phase 2t, Q: phase 2t+1)
+        if constexpr (!IDLE) {
+          load_frags(st, af, bfr);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        if constexpr (GQ) vm_wait<PA>();   // the B tile of tile t + 1, before P reads it
+        phase_end();
+        // multiply tile t; tile t + 2 into stage st (P: its A half in phase
+        // 2t+1; Q: the B tile and its A half in phase 2t+2)
+        if constexpr (!IDLE) {
+          mfmas_spread(af, bfr, std::integral_constant<int, ND>{},
+                       [&](int q) __attribute__((always_inline)) { dma_tile(t + 2, st, q); });
+        } else {
+#pragma unroll
+          for (int q = 0; q < ND; ++q) dma_tile(t + 2, st, q);
+        }
+        vm_wait<GQ ? PB + PA : PA>();   // its A half of tile t + 1
+        phase_end();
+      }
+      if constexpr (!GQ) phase_end();   // Q's last multiply
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (gq) {
+      if (idle) pp_loop(T_{}, T_{});
+      else pp_loop(T_{}, F_{});
+    } else {
+      if (idle) pp_loop(F_{}, T_{});
+      else pp_loop(F_{}, F_{});
+    }
+  } else if constexpr (C::PIPE == 1) {
     // Software pipeline over 32-wide K steps: the fragments of the next step
     // are read from LDS while the MFMAs of the current one run.  One barrier
     // per K tile, before its last step: it publishes tile kt + 1 (every
@@ -550,15 +692,16 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
 }
 
 // Tile shapes (BM x BN, waves WGM x WGN, waves per SIMD, LDS stages, K tile,
-// tile-group divisor).  Forward: 256 x 256 tiles with a 64-wide K tile
-// (128-byte rows per DMA lane group, one 8-wave block per CU): fewer operand
-// bytes per flop and full cache lines outweigh the longer ragged tail
+// tile-group divisor, main loop).  Forward: 256 x 256 tiles with a 64-wide K
+// tile (128-byte rows per DMA lane group, one 8-wave block per CU): fewer
+// operand bytes per flop and full cache lines outweigh the longer ragged tail
 // (measured 8 % faster for both forward GEMMs); tile groups of 8 blocks, a
-// quarter of an XCD's resident blocks (about 2 % faster than 32).  The dgrad
-// kinds measured faster with 128 x 256, K tile 32, two 4-wave blocks per CU,
-// and whole-XCD tile groups.
+// quarter of an XCD's resident blocks (about 2 % faster than 32); the
+// ping-pong loop (GEMM W13 6 % faster at the 30B shape, 11 % at the 235B
+// shape, GEMM W2 1 % and 5 %).  The dgrad kinds measured faster with
+// 128 x 256, K tile 32, two 4-wave blocks per CU, and whole-XCD tile groups.
 #ifndef MOE_CFG_ROW_FWD
-#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64, 4
+#define MOE_CFG_ROW_FWD 256, 256, 2, 4, 2, 2, 64, 4, 2
 #endif
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
