@@ -54,6 +54,9 @@ def test_config1_fp32():
     (mi.LayerDims(T=300, H=256, I=128, E=8, k=2, dtype="bf16"), 101),
     (mi.LayerDims(T=1000, H=384, I=192, E=16, k=4, dtype="bf16"), 102),    # N tail (I=192)
     (mi.LayerDims(T=777, H=512, I=256, E=32, k=8, dtype="bf16", skew=True), 103),
+    # the smallest H and I: the forward GEMMs (ping-pong loop) run a single
+    # 64-wide K tile, the 256-column tiles are mostly tail
+    (mi.LayerDims(T=500, H=64, I=64, E=8, k=2, dtype="bf16"), 104),
 ])
 def test_small_bf16(dims, seed):
     _full_compare(dims, mi.make_inputs(dims, seed), TOL["bf16"])
