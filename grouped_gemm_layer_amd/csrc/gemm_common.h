@@ -71,7 +71,8 @@ struct TileCfg {
   // main loop: 0 = every wave reads a whole K tile's fragments between two
   // barriers, then runs its MFMAs; 1 = software pipeline, the fragments of the
   // next 32-wide K step are read while the MFMAs of the current one run (one
-  // barrier per K tile)
+  // barrier per K tile); 2 = ping-pong between the two wave rows (row kinds
+  // of the bf16 kernel: one row reads a K tile while the other multiplies)
   static constexpr int PIPE = PIPE_;
   static constexpr int WPE = WPE_;      // waves per SIMD the register allocation must allow
   static constexpr int STAGES = ST_;    // LDS stages in flight (>= 2)
