@@ -86,30 +86,26 @@ def hbm_bytes(d):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the library's kernel sources and headers: recorded counter
-    figures apply only while this is unchanged."""
+def kernel_binary_hash() -> str:
+    """sha256 of the built library (its device code included): recorded
+    counter figures apply only to the binary they were taken on."""
+    import grouped_gemm_layer_amd as gl
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "grouped_gemm_layer_amd", "csrc", "*"))
-                   + [os.path.join(ROOT, "include", "moe.h"),
-                      os.path.join(ROOT, "grouped_gemm_layer_amd", "build_lib.py")])
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    with open(gl.lib_path(), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()
 
 
 def recorded_traffic(config: int, kernel: str):
     """HBM bytes per launch of `kernel` from the committed PMC figures
     (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
-    they are missing or were taken on other kernel sources."""
+    they are missing or were taken on another build of the library."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash() or rec.get("config") != config:
+    if rec.get("library_sha256") != kernel_binary_hash() or rec.get("config") != config:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
