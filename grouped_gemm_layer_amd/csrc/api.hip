@@ -62,7 +62,7 @@ Sizes compute_sizes(const moe_dims* d) {
   const size_t M = (size_t)d->T * d->k;
   const size_t es = (d->mode == MOE_MODE_FP32) ? 4 : 2;
   const size_t max_tiles = (size_t)max_row_tiles((int)M, d->E, fwd_row_tile_m(d->mode));
-  const size_t max_tiles_b = (size_t)max_row_tiles((int)M, d->E, bwd_row_tile_m(d->mode));
+  const size_t max_tiles_b = (size_t)max_row_tiles((int)M, d->E, bwd_row_tile_m(d->mode, d->H, d->I));
   const size_t nblk = (size_t)route_num_blocks((int)M);
   size_t o = 0;
   s.r_partials = o; o += align_up(nblk * d->E * 4);
@@ -465,7 +465,7 @@ moe_status backward_impl(const moe_dims* dims, const void* dy, const void* x, co
     a.wpart13 = reinterpret_cast<float*>(at(ws, s.b_wpart13));
     a.wpart2 = reinterpret_cast<float*>(at(ws, s.b_wpart2));
   }
-  const int bm = bwd_row_tile_m(dims->mode);
+  const int bm = bwd_row_tile_m(dims->mode, dims->H, dims->I);
   Mx8Args q = mx8 ? mx8_args(dims, s, ws, saved) : Mx8Args{};
   if (mx8 && wcodes) {   // the caller's transposed weight copies
     const WCodes wc = wcodes_layout(dims);

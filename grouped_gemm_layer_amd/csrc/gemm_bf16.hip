@@ -706,6 +706,17 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
 #ifndef MOE_CFG_ROW
 #define MOE_CFG_ROW 128, 256, 2, 2, 2, 2, 32
 #endif
+// dgrad kinds when both of their K dimensions (H for W2, 2I for W13) reach
+// MOE_DGRAD_LONG_K: 256 x 256 tiles with the ping-pong loop, whose fixed
+// start and end phases then weigh less (Qwen3-235B-A22B shape: dgrad W13
+// 3.26 -> 2.96 ms, dgrad W2 1.92 -> 1.79 ms; at the 30B shape, K = 2048 and
+// 1536, the same tiles were 0-5 % slower than two 128 x 256 blocks per CU)
+#ifndef MOE_CFG_ROW_LONG
+#define MOE_CFG_ROW_LONG 256, 256, 2, 4, 2, 2, 64, 4, 2
+#endif
+#ifndef MOE_DGRAD_LONG_K
+#define MOE_DGRAD_LONG_K 3072
+#endif
 // Weight gradients: two 4-wave blocks per CU (57 KB of LDS each), so that
 // one block's fp32 output stores overlap the other's main loop.  wgrad of W2
 // (M = H, N = I): 128 x 256, wgrad of W13 (M = 2I, N = H): 256 x 128; against
@@ -719,6 +730,8 @@ void gemm_bf16_kernel(LayerArgs a, int n_tiles, int tiles_total, int nvb) {
 #endif
 using CfgRowF = TileCfg<MOE_CFG_ROW_FWD>;
 using CfgRow = TileCfg<MOE_CFG_ROW>;
+using CfgRowL = TileCfg<MOE_CFG_ROW_LONG>;
+static_assert(CfgRowL::BN == CfgRow::BN, "one gate-gradient partial per 256-column tile of the dgrad of W2");
 using CfgW = TileCfg<MOE_CFG_WGRAD>;
 using CfgW1 = TileCfg<MOE_CFG_WGRAD1>;
 
@@ -745,15 +758,17 @@ hipError_t launch_kind(const LayerArgs& a, hipStream_t s) {
 }  // namespace
 
 int bf16_fwd_row_tile_m() { return CfgRowF::BM; }
-int bf16_row_tile_m() { return CfgRow::BM; }
+bool bf16_dgrad_long(int H, int I) { return H >= MOE_DGRAD_LONG_K && 2 * I >= MOE_DGRAD_LONG_K; }
+int bf16_row_tile_m(int H, int I) { return bf16_dgrad_long(H, I) ? CfgRowL::BM : CfgRow::BM; }
 int bf16_dgrad2_tile_n() { return CfgRow::BN; }
 
 hipError_t launch_gemm_bf16(GemmKind kind, const LayerArgs& a, hipStream_t s) {
+  const bool long_k = bf16_dgrad_long(a.H, a.I);
   switch (kind) {
     case KIND_FWD1: return launch_kind<KIND_FWD1, CfgRowF>(a, s);
     case KIND_FWD2: return launch_kind<KIND_FWD2, CfgRowF>(a, s);
-    case KIND_DGRAD2: return launch_kind<KIND_DGRAD2, CfgRow>(a, s);
-    case KIND_DGRAD1: return launch_kind<KIND_DGRAD1, CfgRow>(a, s);
+    case KIND_DGRAD2: return long_k ? launch_kind<KIND_DGRAD2, CfgRowL>(a, s) : launch_kind<KIND_DGRAD2, CfgRow>(a, s);
+    case KIND_DGRAD1: return long_k ? launch_kind<KIND_DGRAD1, CfgRowL>(a, s) : launch_kind<KIND_DGRAD1, CfgRow>(a, s);
     case KIND_WGRAD2: return launch_kind<KIND_WGRAD2, CfgW>(a, s);
     case KIND_WGRAD1: return launch_kind<KIND_WGRAD1, CfgW1>(a, s);
   }

@@ -254,7 +254,8 @@ hipError_t launch_mx_quant_tokens_t(const T* src, int F, const int32_t* s2f, int
 
 // tiling the API layer needs for workspace sizing and the tile table
 int bf16_fwd_row_tile_m();  // token rows per tile of the bf16 forward GEMMs
-int bf16_row_tile_m();      // token rows per tile of the bf16 dgrad GEMMs
+bool bf16_dgrad_long(int H, int I);  // the bf16 dgrad GEMMs take their long-K tiles
+int bf16_row_tile_m(int H, int I);   // token rows per tile of the bf16 dgrad GEMMs
 int bf16_dgrad2_tile_n();   // columns per tile of the bf16 dgrad of W2
 constexpr int FP32_BM = 64;
 constexpr int FP32_BN = 64;
@@ -300,8 +301,8 @@ int resident_blocks(int per_cu);
 inline int fwd_row_tile_m(int mode) {
   return mode == 0 ? FP32_BM : mx8_forward(mode) ? mx8_fwd_row_tile_m() : bf16_fwd_row_tile_m();
 }
-inline int bwd_row_tile_m(int mode) {
-  return mode == 0 ? FP32_BM : mx8_backward(mode) ? mx8_row_tile_m() : bf16_row_tile_m();
+inline int bwd_row_tile_m(int mode, int H, int I) {
+  return mode == 0 ? FP32_BM : mx8_backward(mode) ? mx8_row_tile_m() : bf16_row_tile_m(H, I);
 }
 inline int dgrad2_parts(int mode, int I) {
   // N tiles of the dgrad of W2 (N = I): one gate-gradient partial per tile

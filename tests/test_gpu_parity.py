@@ -57,6 +57,10 @@ def test_config1_fp32():
     # the smallest H and I: the forward GEMMs (ping-pong loop) run a single
     # 64-wide K tile, the 256-column tiles are mostly tail
     (mi.LayerDims(T=500, H=64, I=64, E=8, k=2, dtype="bf16"), 104),
+    # the 235B expert shape (both dgrad K dimensions >= 3072): the dgrad GEMMs
+    # take their 256-row ping-pong tiles; experts of about 75 rows leave the
+    # second wave row of every tile idle
+    (mi.LayerDims(T=300, H=4096, I=1536, E=8, k=2, dtype="bf16"), 105),
 ])
 def test_small_bf16(dims, seed):
     _full_compare(dims, mi.make_inputs(dims, seed), TOL["bf16"])
