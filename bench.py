@@ -425,6 +425,47 @@ def time_extra(g, mi, cfg, mode, base, K, W, ev):
     return out
 
 
+def token_sweep(g, d, tokens, K, W):
+    """Route + forward + backward of the shape (H, I, E, k) of `d` at other
+    token counts, bf16, K timed steps after W untimed ones (device clock
+    around the whole region).  `weight_floor_ms` is the time HBM needs for the
+    weight traffic alone at 8 TB/s: every bf16 weight read by the forward and
+    by the dgrad GEMMs, the fp32 weight gradients written once; below a few
+    hundred rows per expert a step approaches it."""
+    import torch
+    H, I, E, k = d.H, d.I, d.E, d.k
+    w_elems = E * 3 * H * I
+    floor_ms = (2 * 2 * w_elems + 4 * w_elems) / (PEAK_HBM_GBS * 1e9) * 1e3
+    out = []
+    for T in tokens:
+        gen = torch.Generator(device="cuda").manual_seed(T)
+        bf = torch.bfloat16
+        x = torch.randn(T, H, device="cuda", generator=gen).to(bf)
+        w13 = (torch.randn(E, 2 * I, H, device="cuda", generator=gen) * 0.02).to(bf)
+        w2 = (torch.randn(E, H, I, device="cuda", generator=gen) * 0.02).to(bf)
+        logits = torch.randn(T, E, device="cuda", generator=gen)
+        dy = torch.randn(T, H, device="cuda", generator=gen).to(bf)
+        layer = g.MoeLayer(T, H, I, E, k, mode="bf16")
+
+        def step():
+            layer.route(logits)
+            layer.forward(x, w13, w2)
+            layer.backward(dy, x, w13, w2)
+        for _ in range(W):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / K
+        out.append({"T": T, "rows_per_expert": T * k / E, "ms_per_step": round(ms, 4),
+                    "tflops": round(18.0 * T * k * H * I / ms / 1e9, 1), "weight_floor_ms": round(floor_ms, 4)})
+        del layer, x, w13, w2, logits, dy
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -445,6 +486,9 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=10, help="timed steps per extra workload")
     ap.add_argument("--vendor-ceiling", action="store_true",
                     help="also time hipBLASLt on the per-expert GEMM shapes (roofline context)")
+    ap.add_argument("--token-sweep", type=str, default="",
+                    help="comma-separated token counts: also time route + forward + backward of the "
+                         "configuration's shape at each (bf16 mode, seeded random inputs on the device)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the timed region (counter calibration)")
     args = ap.parse_args()
@@ -511,6 +555,10 @@ def main():
         out["ms_checkpointed_step"] = round(out["route_ms"] + nosave + rec + out["bwd_ms"], 4)
     if args.vendor_ceiling:
         out["vendor_ceiling"] = vendor_ceiling(d)
+    if args.token_sweep:
+        layer = None
+        torch.cuda.empty_cache()
+        out["token_sweep"] = token_sweep(g, d, [int(v) for v in args.token_sweep.split(",")], K, W)
     if not args.no_extras and not args.no_workloads and args.config == 2 and args.mode is None:
         del layer
         torch.cuda.empty_cache()
